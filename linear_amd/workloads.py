@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs for the FP16 linear layer.
+
+This module only draws random numbers and lays out tensors; it holds none of
+the layer's arithmetic, so both the HIP path's tests and the CPU oracle's tests
+take their inputs from here.
+
+Recipe (one ``torch.Generator('cpu')`` per workload, seeded; draws in the order
+x, weight, b, each drawn in float32 and converted to float16 with torch's
+round-to-nearest-even conversion):
+
+    x      ~ N(0, 1)                     shape [M, K]
+    weight ~ U(-a, a) = (2u - 1) * a      shape [N, K]   ([out_features, in_features])
+    b      ~ U(-a, a)                     shape [N]
+
+The toy workload's shapes are the ones of "tensor programs, part 1" (the
+PyTorch line that builds x [1024, 768], weight [1024, 768], b [1024]); its bound
+a = 1/sqrt(768) is nn.Linear's default initialisation bound for 768 input
+features (the page names nn.Linear(768, 1024)).  The other workloads are
+decode- and prefill-shaped projections of a 4096-wide model.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    a: float          # half-width of the uniform law of weight and b
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        """Algorithmic FLOPs of the contraction: one multiply and one add per (m, n, k)."""
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: x, weight and b read once, y written once (2 B each)."""
+        return 2 * (self.M * self.K + self.N * self.K + self.N + self.M * self.N)
+
+
+WORKLOADS = {
+    "toy": Workload("toy", 1024, 1024, 768, 1.0 / math.sqrt(768.0),
+                    "toy linear of the pages: x[1024,768] @ weight[1024,768].T + b[1024]"),
+    "gemv1": Workload("gemv1", 1, 4096, 4096, 1.0 / 64.0, "decode GEMV, one row"),
+    "gemv16": Workload("gemv16", 16, 4096, 4096, 1.0 / 64.0, "decode GEMV batch, 16 rows"),
+    "attn": Workload("attn", 8192, 4096, 4096, 1.0 / 64.0, "prefill attention projection"),
+    "mlp_up": Workload("mlp_up", 4096, 14336, 4096, 1.0 / 64.0, "prefill MLP up-projection"),
+    "down": Workload("down", 2000, 4000, 14336, 1.0 / math.sqrt(14336.0),
+                     "deep-K down-projection, M and N not multiples of a tile"),
+}
+
+# The decode batch: one step runs both decode shapes over the same weight size.
+DECODE_STEP = ("gemv1", "gemv16")
+
+
+def make_inputs(M: int, N: int, K: int, a: float, seed: int = 0, device: str = "cpu"):
+    """Draw (x, weight, b) as contiguous float16 tensors, following the recipe above."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn((M, K), generator=g, dtype=torch.float32)
+    w = torch.rand((N, K), generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0).mul_(a)
+    b = torch.rand((N,), generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0).mul_(a)
+    x16, w16, b16 = x.to(torch.float16), w.to(torch.float16), b.to(torch.float16)
+    if device != "cpu":
+        x16, w16, b16 = x16.to(device), w16.to(device), b16.to(device)
+    return x16, w16, b16
+
+
+def workload_inputs(name: str, seed: int = 0, device: str = "cpu"):
+    wl = WORKLOADS[name]
+    return make_inputs(wl.M, wl.N, wl.K, wl.a, seed=seed, device=device)
+
+
+def small_integers(M: int, N: int, K: int, seed: int = 0, lo: int = -3, hi: int = 3,
+                   blo: int = -8, bhi: int = 8):
+    """Integer-valued float16 tensors: x, weight in [lo, hi], b in [blo, bhi].
+
+    With sum |x*w| < 2^24 every partial sum in every order is an exact FP32
+    integer, so the result is unique whatever the summation order."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float16)
+    w = torch.randint(lo, hi + 1, (N, K), generator=g).to(torch.float16)
+    b = torch.randint(blo, bhi + 1, (N,), generator=g).to(torch.float16)
+    return x, w, b
+
+
+def random_words(shape, seed: int = 0, finite: bool = True):
+    """Uniformly random binary16 bit patterns (optionally finite only) as float16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    words = torch.randint(0, 1 << 16, shape, generator=g, dtype=torch.int32)
+    if finite:
+        # exponent field 31 is inf/NaN: clear its top bit so the field becomes 15
+        e31 = (words & 0x7C00) == 0x7C00
+        words = torch.where(e31, words & ~0x4000, words)
+    return words.to(torch.int16).view(torch.float16)
+
+
+def sample_points(M: int, N: int, count: int, seed: int = 0):
+    """Output coordinates for full-size spot checks: the four corners, the last
+    row and column (ragged edges), and uniform random (m, n) pairs."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 7919)
+    ms = torch.randint(0, M, (count,), generator=g)
+    ns = torch.randint(0, N, (count,), generator=g)
+    edge_m = torch.tensor([0, 0, M - 1, M - 1] + [M - 1] * 64 + list(range(min(M, 64))))
+    edge_n = torch.tensor([0, N - 1, 0, N - 1] + torch.randint(0, N, (64,), generator=g).tolist()
+                          + [N - 1] * min(M, 64))
+    return torch.cat([edge_m, ms]).numpy(), torch.cat([edge_n, ns]).numpy()

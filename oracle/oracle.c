@@ -1,0 +1,281 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * The plain, slow, obviously correct CPU definition of the FP16 linear layer
+ *
+ *     proj[m,n] = FP16( sum_k x[m,k] * weight[n,k] )      (FP32 accumulation)
+ *     y[m,n]    = FP16( FP32(proj[m,n]) + FP32(b[n]) )
+ *
+ * as fixed by "tensor programs, part 1", section "One Program and One Numerical
+ * Contract" (the contraction formula and its two numbered requirements: FP32
+ * matrix arithmetic with products not rounded to FP16, any summation order;
+ * the projection rounded to FP16 before the bias is added, output FP16) and by
+ * the Inductor capture in section "Inductor Retains MatMul and Explicit Casts"
+ * (the rounded mm result and the bias are both widened to f32, added in f32,
+ * and the sum is converted back to f16).
+ *
+ * Nothing on the GPU path calls, links or includes this file.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no source with the HIP library: every conversion below is written out
+ * from the IEEE 754 binary16 / binary32 encodings, not taken from a compiler
+ * intrinsic or a library.
+ *
+ * Readings where the pages are silent (all listed in the design notes):
+ *   - "rounded to FP16" is IEEE roundTiesToEven, with gradual underflow
+ *     (subnormals kept) and overflow to infinity;
+ *   - of the many summation orders the contract allows, the oracle takes the
+ *     plain sequential one, k = 0, 1, ..., K-1, starting from +0;
+ *   - K == 0 is the empty sum (+0).
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (no reassociation; an FMA would give the same bits anyway because every
+ * product of two binary16 values is exact in binary32).
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------------
+ * binary16 -> binary32, from the encoding: 1 sign bit, 5 exponent bits (bias
+ * 15), 10 fraction bits.  Exponent field 0 is zero/subnormal (value
+ * fraction * 2^-24), field 31 is infinity/NaN.  Every binary16 value is exactly
+ * representable in binary32, so this is exact.
+ * ------------------------------------------------------------------------- */
+static float f32_from_bits(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t bits_from_f32(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+float oracle_f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t e = (uint32_t)(h >> 10) & 0x1fu;
+    uint32_t frac = (uint32_t)h & 0x3ffu;
+    float mag;
+    if (e == 0u) {
+        /* zero or subnormal: frac * 2^-24; frac < 2^10 so the product is exact */
+        mag = ldexpf((float)frac, -24);
+    } else if (e == 31u) {
+        if (frac == 0u) {
+            mag = f32_from_bits(0x7f800000u);                       /* infinity */
+        } else {
+            /* NaN: keep it quiet, carry the fraction into the top bits */
+            mag = f32_from_bits(0x7fc00000u | (frac << 13));
+        }
+    } else {
+        /* normal: (1024 + frac) * 2^(e - 25) */
+        mag = ldexpf((float)(1024u + frac), (int)e - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+/* ---------------------------------------------------------------------------
+ * binary32 -> binary16, round to nearest, ties to even.
+ *
+ * A finite non-zero binary32 value is s * 2^(e-23) with s a 24-bit integer in
+ * [2^23, 2^24) (normal) -- binary32 subnormals are below 2^-126, far under half
+ * of the smallest binary16 subnormal (2^-25), so they round to zero.  The
+ * binary16 grid has spacing 2^(e-10) for e >= -14 and 2^-24 below that.  We
+ * express the value in units of the target spacing, split off the integer part
+ * q and the discarded remainder, and round: up if the remainder is more than
+ * half a unit, or exactly half and q is odd.
+ * ------------------------------------------------------------------------- */
+uint16_t oracle_f32_to_f16(float f) {
+    uint32_t u = bits_from_f32(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t be = (u >> 23) & 0xffu;
+    uint32_t frac = u & 0x7fffffu;
+
+    if (be == 0xffu) {
+        if (frac == 0u) return (uint16_t)(sign | 0x7c00u);          /* +-inf */
+        return (uint16_t)(sign | 0x7e00u | (frac >> 13));            /* quiet NaN */
+    }
+    if (be == 0u) return sign;                   /* +-0 and binary32 subnormals */
+
+    int e = (int)be - 127;                       /* value = s * 2^(e-23) */
+    uint32_t s = frac | 0x800000u;
+    if (e >= 16) return (uint16_t)(sign | 0x7c00u);   /* >= 2^16: overflow */
+
+    int shift;        /* number of low bits of s below the target spacing */
+    int normal = (e >= -14);
+    if (normal) {
+        shift = 13;                              /* spacing 2^(e-10) = 2^13 units of 2^(e-23) */
+    } else {
+        shift = -e - 1;                          /* spacing 2^-24: 2^(-24-(e-23)) = 2^(-e-1) */
+        if (shift >= 25) return sign;            /* value < 2^-25 ... strictly below half: 0 */
+    }
+    uint32_t q = s >> shift;
+    uint32_t rem = s & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u;
+
+    if (normal) {
+        /* q in [1024, 2048]; 2048 means the significand carried into the next binade */
+        if (q == 2048u) { q = 1024u; e += 1; }
+        if (e >= 16) return (uint16_t)(sign | 0x7c00u);
+        return (uint16_t)(sign | (uint16_t)(((uint32_t)(e + 15) << 10) | (q - 1024u)));
+    }
+    /* subnormal: q in [0, 1024]; q == 1024 is exactly the smallest normal, whose
+       encoding (exponent field 1, fraction 0) is the integer 1024 itself */
+    return (uint16_t)(sign | (uint16_t)q);
+}
+
+void oracle_f16_to_f32_array(const uint16_t* h, float* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f32(h[i]);
+}
+
+void oracle_f32_to_f16_array(const float* f, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_f16(f[i]);
+}
+
+/* The bias epilogue, one element: widen the rounded projection and the bias to
+   FP32, add in FP32, round the sum to FP16 (Inductor capture's cast sequence). */
+uint16_t oracle_bias_epilogue(uint16_t proj16, uint16_t b16) {
+    float s = oracle_f16_to_f32(proj16) + oracle_f16_to_f32(b16);
+    return oracle_f32_to_f16(s);
+}
+
+void oracle_bias_epilogue_array(const uint16_t* p, const uint16_t* b, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bias_epilogue(p[i], b[i]);
+}
+
+/* The FP32 accumulation for one output element: sequential k order from +0.
+   Each product of two binary16 values is exact in binary32 (11 + 11 significand
+   bits, exponents within range), so only the additions round. */
+static float dot_f32(const float* xr, const float* wr, int64_t K) {
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) acc = acc + xr[k] * wr[k];
+    return acc;
+}
+
+/* Widen a row-major [rows, cols] binary16 matrix with row stride ld to a dense
+   FP32 copy (test-side only; the GPU path never widens). */
+static float* widen(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols) {
+    float* dst = (float*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(cols > 0 ? cols : 1) * sizeof(float));
+    if (!dst) return NULL;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) dst[r * cols + c] = oracle_f16_to_f32(src[r * ld + c]);
+    return dst;
+}
+
+/*
+ * Full oracle.  x: [M,K] row stride ldx; w: [N,K] row stride ldw (the
+ * [out_features, in_features] weight, contracted over its second axis, i.e. the
+ * transposed weight is a view); b: [N] or NULL; outputs y and proj: [M,N] row
+ * stride ldy (either may be NULL).  With b == NULL, y = proj.
+ * nthreads <= 0 uses the OpenMP default.  Returns 0, or -1 on allocation failure.
+ */
+int oracle_linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                      const uint16_t* b, uint16_t* y, uint16_t* proj, int64_t ldy,
+                      int64_t M, int64_t N, int64_t K, int nthreads) {
+    if (M <= 0 || N <= 0) return 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    float* xf = widen(x, ldx, M, K);
+    float* wf = widen(w, ldw, N, K);
+    if (!xf || !wf) { free(xf); free(wf); return -1; }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = dot_f32(xf + m * K, wf + n * K, K);
+            uint16_t p16 = oracle_f32_to_f16(acc);
+            if (proj) proj[m * ldy + n] = p16;
+            if (y) y[m * ldy + n] = b ? oracle_bias_epilogue(p16, b[n]) : p16;
+        }
+    }
+    free(xf);
+    free(wf);
+    return 0;
+}
+
+/*
+ * The same definition evaluated at a list of output coordinates (ms[i], ns[i]),
+ * for full-size problems where the whole triple loop would take minutes.  Any of
+ * the outputs may be NULL.  S and A are the FP64 band data: S = sum_k x*w and
+ * A = sum_k |x*w|, each product exact in FP64 (used by the tolerance rule).
+ */
+void oracle_linear_f16_points(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                              const uint16_t* b, int64_t K, const int64_t* ms, const int64_t* ns,
+                              int64_t count, uint16_t* y_out, uint16_t* proj_out,
+                              double* S_out, double* A_out, int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        const uint16_t* xr = x + ms[i] * ldx;
+        const uint16_t* wr = w + ns[i] * ldw;
+        float acc = 0.0f;
+        double S = 0.0, A = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            float xv = oracle_f16_to_f32(xr[k]);
+            float wv = oracle_f16_to_f32(wr[k]);
+            acc = acc + xv * wv;
+            double pd = (double)xv * (double)wv;
+            S += pd;
+            A += fabs(pd);
+        }
+        uint16_t p16 = oracle_f32_to_f16(acc);
+        if (proj_out) proj_out[i] = p16;
+        if (y_out) y_out[i] = b ? oracle_bias_epilogue(p16, b[ns[i]]) : p16;
+        if (S_out) S_out[i] = S;
+        if (A_out) A_out[i] = A;
+    }
+}
+
+/* FP64 band data for a whole [M,N] output (small problems only). */
+int oracle_band_f64(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                    int64_t M, int64_t N, int64_t K, double* S, double* A, int nthreads) {
+    if (M <= 0 || N <= 0) return 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    float* xf = widen(x, ldx, M, K);
+    float* wf = widen(w, ldw, N, K);
+    if (!xf || !wf) { free(xf); free(wf); return -1; }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double pd = (double)xf[m * K + k] * (double)wf[n * K + k];
+                s += pd;
+                a += fabs(pd);
+            }
+            S[m * N + n] = s;
+            A[m * N + n] = a;
+        }
+    }
+    free(xf);
+    free(wf);
+    return 0;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP16 linear layer y = FP16(FP16(x @ weight.T) + b) on one MI355X.
+
+One step is the decode-shaped GEMV batch: the layer at x [1, 4096] and at
+x [16, 4096], each against a [4096, 4096] weight and a [4096] bias (both calls
+go through the library's automatic path choice, i.e. the skinny
+weight-streaming kernel).  The metric is HBM GB/s from algorithmic bytes
+(x, weight and b read once, y written once).  Weight copies rotate over more
+than 512 MiB so the 256 MB Infinity Cache cannot serve a weight from a previous
+call.  Inputs are synthetic, seeded, resident in HBM before timing starts.
+
+The line also carries, under "prefill", the MFMA-bound shapes (toy 1024x1024x768,
+attention projection 8192x4096x4096, MLP up-projection 4096x14336x4096, ragged
+down-projection 2000x4000x14336) in TFLOP/s against the FP16 dense MFMA peak,
+and, under "cpu_baseline", the CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense FP16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+ROTATE_BYTES = 512 * 1024 * 1024
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--repeats", type=int, default=5, help="timed regions; the median is reported")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
+    return ap.parse_args()
+
+
+def rotation_sets(bytes_per_set: int) -> int:
+    return max(2, math.ceil(ROTATE_BYTES / max(bytes_per_set, 1)))
+
+
+def capture(fn, calls, stream, torch):
+    """Capture fn(0) .. fn(calls-1) into one HIP graph on `stream` (launch overhead of
+    Python and ctypes stays out of the timed region; the kernels allocate nothing
+    and issue no memset, so they replay unchanged)."""
+    with torch.cuda.stream(stream):
+        for i in range(calls):      # eager warm-up on the capture stream
+            fn(i)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(calls):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_region(graph, replays, stream, torch):
+    """Replay `graph` `replays` times between two HIP events on `stream`; return ms."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end)
+
+
+def bench_decode(args, torch, la, workloads, stream):
+    """The step: one call at M=1 and one at M=16.  Returns (ms_per_step, detail)."""
+    w1, w16 = workloads.WORKLOADS["gemv1"], workloads.WORKLOADS["gemv16"]
+    x1, wbase, b = workloads.workload_inputs("gemv1", seed=0, device="cuda")
+    x16, _, _ = workloads.workload_inputs("gemv16", seed=0, device="cuda")
+    copies = rotation_sets(wbase.numel() * 2)
+    weights = [wbase] + [wbase.clone() for _ in range(copies - 1)]
+    y1 = torch.empty((1, w1.N), dtype=torch.float16, device="cuda")
+    y16 = torch.empty((16, w16.N), dtype=torch.float16, device="cuda")
+    step_bytes = w1.bytes + w16.bytes
+
+    def step(i):
+        la.linear_f16(x1, weights[(2 * i) % copies], b, out=y1, stream=stream)
+        la.linear_f16(x16, weights[(2 * i + 1) % copies], b, out=y16, stream=stream)
+
+    # one graph holds `period` steps, so every weight copy is used once per replay
+    period = max(1, copies // 2)
+    graph = capture(step, period, stream, torch)
+    replays = max(1, args.steps // period)
+    steps = replays * period
+    for _ in range(max(1, args.warmup // period)):
+        graph.replay()
+    times = [time_region(graph, replays, stream, torch) for _ in range(args.repeats)]
+    ms = sorted(times)[len(times) // 2] / steps
+    args.steps = steps
+    plan = la.linear_f16_plan(x16, wbase, b)
+    detail = {
+        "step_bytes": step_bytes,
+        "weight_copies": copies,
+        "steps_per_graph": period,
+        "ms_per_step_all": [t / steps for t in times],
+        "plan_m16": plan,
+        "plan_m1": la.linear_f16_plan(x1, wbase, b),
+    }
+    return ms, detail
+
+
+def bench_gemm(name, torch, la, workloads, stream, calls):
+    wl = workloads.WORKLOADS[name]
+    x, w, b = workloads.workload_inputs(name, seed=0, device="cuda")
+    sets = rotation_sets(wl.bytes)
+    xs = [x] + [x.clone() for _ in range(sets - 1)]
+    ws = [w] + [w.clone() for _ in range(sets - 1)]
+    ys = [torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda") for _ in range(sets)]
+
+    def call(i):
+        k = i % sets
+        la.linear_f16(xs[k], ws[k], b, out=ys[k], stream=stream)
+
+    graph = capture(call, sets, stream, torch)
+    replays = max(1, calls // sets)
+    graph.replay()
+    times = [time_region(graph, replays, stream, torch) for _ in range(5)]
+    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    del graph
+    tflops = wl.flops / (ms * 1e-3) / 1e12
+    plan = la.linear_f16_plan(x, w, b)
+    del xs, ws, ys
+    return {
+        "M": wl.M, "N": wl.N, "K": wl.K,
+        "us_per_call": round(ms * 1e3, 3),
+        "tflops": round(tflops, 1),
+        "frac_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "hbm_gbs_algorithmic": round(wl.bytes / (ms * 1e-3) / 1e9, 1),
+        "input_sets": sets,
+        "tile": [plan["tile_m"], plan["tile_n"]],
+        "grid": plan["grid"],
+    }
+
+
+def cpu_baseline(workloads, target_s: float = 10.0):
+    """The CPU oracle on the same decode step, repeated until ~target_s of CPU work."""
+    import oracle
+    orc = oracle.default()
+    x1, w, b = workloads.workload_inputs("gemv1", seed=0)
+    x16, _, _ = workloads.workload_inputs("gemv16", seed=0)
+    step_bytes = workloads.WORKLOADS["gemv1"].bytes + workloads.WORKLOADS["gemv16"].bytes
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.linear(x1, w, b)
+        orc.linear(x16, w, b)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 200:
+            break
+    per_step = el / reps
+    return {
+        "value": round(step_bytes / per_step / 1e9, 3),
+        "unit": "GB/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": "%d full decode steps (x[1,4096] and x[16,4096] against weight[4096,4096] + b), "
+                  "%.1f s wall, %.1f ms per step" % (reps, el, per_step * 1e3),
+        "ms_per_step": round(per_step * 1e3, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_amd as la
+    from linear_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    la._lib()
+    stream = torch.cuda.Stream()
+    log("device:", torch.cuda.get_device_name(0))
+
+    if args.only:
+        if args.only == "decode":
+            ms, _ = bench_decode(args, torch, la, workloads, stream)
+            log("decode ms/step %.5f" % ms)
+        else:
+            log(json.dumps(bench_gemm(args.only, torch, la, workloads, stream, 100)))
+        return
+
+    log("decode step: %d warmup, %d timed x %d repeats" % (args.warmup, args.steps, args.repeats))
+    ms, detail = bench_decode(args, torch, la, workloads, stream)
+    step_bytes = detail["step_bytes"]
+    value = step_bytes / (ms * 1e-3) / 1e9
+    launches = 2
+    per_launch_bytes = step_bytes / launches
+    per_launch_s = ms * 1e-3 / launches
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    log("decode: %.3f us/step, %.1f GB/s" % (ms * 1e3, value))
+
+    prefill = {}
+    if not args.no_prefill:
+        for name, calls in (("toy", 400), ("attn", 50), ("mlp_up", 30), ("down", 50)):
+            log("prefill", name)
+            prefill[name] = bench_gemm(name, torch, la, workloads, stream, calls)
+            log(json.dumps(prefill[name]))
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(workloads)
+        log(json.dumps(cpu))
+
+    line = {
+        "metric": "HBM GB/s and % peak (M<=16 decode GEMV batch); TFLOP/s and % FP16 MFMA peak (large M)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 accumulate)",
+        "data": "synthetic (seeded: x~N(0,1), weight,b~U(-1/64,1/64))",
+        "config": {
+            "workload": "decode GEMV batch: y=FP16(FP16(x@W.T)+b), x [1,4096] and [16,4096], "
+                        "W [4096,4096], b [4096], fp16",
+            "calls_per_step": launches,
+            "weight_copies_rotated": detail["weight_copies"],
+            "kernel": "skinny_f16_kernel (16x16 tile, 8 waves, v_mfma_f32_16x16x32_f16)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "skinny_f16_kernel",
+            "bytes_per_launch": per_launch_bytes,
+            "us_per_launch": round(per_launch_s * 1e6, 3),
+        },
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * linear_amd.h -- C ABI of the MI355X (gfx950) FP16 linear layer.
+ *
+ *     proj[m,n] = FP16( sum_k x[m,k] * weight[n,k] )     products exact, FP32 accumulation
+ *     y[m,n]    = FP16( FP32(proj[m,n]) + FP32(b[n]) )
+ *
+ * This is the computation and numerical contract of "tensor programs, part 1":
+ * the PyTorch line y = torch.matmul(x, weight.T) + b and Figure 1.1 (the weight
+ * transpose is a view, the projection is rounded before the bias add), the
+ * contraction formula of section "One Program and One Numerical Contract" and its
+ * two requirements (FP32 accumulation of unrounded products in any order; the
+ * projection rounded to FP16 before the bias addition, output FP16), and the
+ * Inductor capture's epilogue (both operands widened to f32, added, rounded to
+ * f16).  The weight is contracted in its stored [N, K] order with no transposed or
+ * widened copy, as the poot Graph IR op table describes a dense contraction.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Binary16 values are passed as uint16_t words (their IEEE 754 bit patterns).
+ *  - x is [M, K] with row stride ldx >= K, weight is [N, K] with row stride
+ *    ldw >= K (the [out_features, in_features] layout), y is [M, N] with row
+ *    stride ldy >= N; strides are in elements, the inner stride is 1.  b is [N],
+ *    contiguous.
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    neither allocates, frees nor keeps them after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream)
+ *    and the call returns without synchronising.  Results are visible after the
+ *    stream is synchronised.
+ *  - Only y[m, n] for m < M, n < N is written; stride padding is never touched.
+ *  - Rounding is IEEE round-to-nearest-even with subnormals kept (no flush to
+ *    zero) and overflow to infinity; the empty sum (K == 0) is +0.
+ *  - For given shapes, the bias call and the bias-less call use the same
+ *    summation order, so y of the bias call equals FP16(FP32(p) + FP32(b)) where
+ *    p is the bias-less result, bit for bit.  Reruns are bit-identical.
+ *  - Every argument error is detected on the host before anything is enqueued;
+ *    y is then untouched.  No exception or abort crosses this ABI.
+ *  - Limits: M, N, K < 2^31; ldx, ldw < 2^22 and ldy < 2^31 elements.
+ *  - Fast path: x and weight 16-byte aligned, ldx, ldw and K multiples of 8.
+ *    Any other layout is accepted and runs a slower element-wise loader.
+ */
+#ifndef LINEAR_AMD_H
+#define LINEAR_AMD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LINEAR_OK         0
+#define LINEAR_E_NULL     1  /* a required pointer is NULL (only when the output is non-empty) */
+#define LINEAR_E_SHAPE    2  /* M, N or K negative, or beyond the limits above */
+#define LINEAR_E_STRIDE   3  /* ldx < K, ldw < K, ldy < N, or a stride beyond its limit */
+#define LINEAR_E_ALIAS    4  /* y's byte range overlaps x, weight or b */
+#define LINEAR_E_PATH     5  /* unknown path selector */
+#define LINEAR_E_DEVICE   6  /* no usable gfx950 device current, or a HIP query failed */
+#define LINEAR_E_LAUNCH   7  /* a kernel launch failed; linear_last_hip_error() has the HIP code */
+
+/* Path selectors for linear_f16_ex / linear_f16_plan. */
+#define LINEAR_PATH_AUTO   0  /* M <= 16: skinny path; otherwise the MFMA tiled GEMM */
+#define LINEAR_PATH_GEMM   1  /* force the MFMA tiled GEMM (any M) */
+#define LINEAR_PATH_SKINNY 2  /* force the weight-streaming skinny path (any M, 16 rows per block) */
+
+/*
+ * y = FP16(FP16(x . weight^T) + b).  See the conventions above.
+ * M == 0 or N == 0 is a successful no-op (pointers may then be NULL).
+ * Returns LINEAR_OK or one of the LINEAR_E_* codes.
+ */
+int32_t linear_f16(const uint16_t* x, int64_t ldx,
+                   const uint16_t* weight, int64_t ldw,
+                   const uint16_t* b,
+                   uint16_t* y, int64_t ldy,
+                   int64_t M, int64_t N, int64_t K,
+                   void* stream);
+
+/*
+ * The projection alone: y = FP16(x . weight^T), no bias.  Same conventions.
+ */
+int32_t linear_f16_nobias(const uint16_t* x, int64_t ldx,
+                          const uint16_t* weight, int64_t ldw,
+                          uint16_t* y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K,
+                          void* stream);
+
+/*
+ * linear_f16 with an explicit path (LINEAR_PATH_*) and an optional bias
+ * (b == NULL computes the projection alone).  Every path gives results within
+ * the same contract; forcing one lets tests exercise both on every shape.
+ */
+int32_t linear_f16_ex(const uint16_t* x, int64_t ldx,
+                      const uint16_t* weight, int64_t ldw,
+                      const uint16_t* b,
+                      uint16_t* y, int64_t ldy,
+                      int64_t M, int64_t N, int64_t K,
+                      int32_t path, void* stream);
+
+/* Which kernel a call would launch.  Pure host function: touches no device. */
+typedef struct linear_plan {
+    int32_t path;       /* LINEAR_PATH_GEMM or LINEAR_PATH_SKINNY */
+    int32_t tile_m;     /* output rows (m) per workgroup */
+    int32_t tile_n;     /* output columns (n) per workgroup */
+    int32_t tile_k;     /* K elements per main-loop stage (GEMM) or per wave step (skinny) */
+    int32_t threads;    /* threads per workgroup */
+    int32_t vector_io;  /* 1: 16-byte loads; 0: element-wise loader */
+    int64_t grid;       /* workgroups launched */
+} linear_plan;
+
+/*
+ * Fill *plan for a call with these shapes, strides, alignments and path, after
+ * the same validation as linear_f16_ex (device pointers are only inspected for
+ * alignment, never dereferenced).  Returns LINEAR_OK or a LINEAR_E_* code.
+ */
+int32_t linear_f16_plan(const uint16_t* x, int64_t ldx,
+                        const uint16_t* weight, int64_t ldw,
+                        const uint16_t* b,
+                        uint16_t* y, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K,
+                        int32_t path, linear_plan* plan);
+
+/* Static English text for a status code (never NULL). */
+const char* linear_status_string(int32_t status);
+
+/* The hipError_t of the last LINEAR_E_DEVICE / LINEAR_E_LAUNCH on this thread (0 if none). */
+int32_t linear_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINEAR_AMD_H */

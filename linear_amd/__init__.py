@@ -1,0 +1,193 @@
+"""MI355X (gfx950) FP16 linear layer: y = FP16(FP16(x @ weight.T) + b).
+
+A thin ctypes binding over the C ABI of ``liblinear_amd.so`` (declared in
+``include/linear_amd.h``).  The functions carry the C entry points' names and
+only marshal arguments: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the stream.  If the library
+is missing the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinear_amd.so")
+
+LINEAR_OK = 0
+LINEAR_E_NULL = 1
+LINEAR_E_SHAPE = 2
+LINEAR_E_STRIDE = 3
+LINEAR_E_ALIAS = 4
+LINEAR_E_PATH = 5
+LINEAR_E_DEVICE = 6
+LINEAR_E_LAUNCH = 7
+
+PATH_AUTO = 0
+PATH_GEMM = 1
+PATH_SKINNY = 2
+
+ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_plan",
+                "linear_status_string", "linear_last_hip_error")
+
+
+class LinearError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s failed: %s (status %d%s)" % (
+            what, linear_status_string(code), code,
+            ", hip error %d" % _lib().linear_last_hip_error()
+            if code in (LINEAR_E_DEVICE, LINEAR_E_LAUNCH) else ""))
+
+
+class LinearArgumentError(LinearError, ValueError):
+    pass
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32), ("vector_io", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def _lib():
+    """Load liblinear_amd.so (after torch, so both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("liblinear_amd.so is not built (run `python -m linear_amd.build` or "
+                           "__graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.linear_f16.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
+    lib.linear_f16.restype = i32
+    lib.linear_f16_nobias.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.linear_f16_nobias.restype = i32
+    lib.linear_f16_ex.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.linear_f16_ex.restype = i32
+    lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
+                                    ctypes.POINTER(_Plan)]
+    lib.linear_f16_plan.restype = i32
+    lib.linear_status_string.argtypes = [i32]
+    lib.linear_status_string.restype = ctypes.c_char_p
+    lib.linear_last_hip_error.argtypes = []
+    lib.linear_last_hip_error.restype = i32
+    _LIB = lib
+    return lib
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def linear_status_string(code: int) -> str:
+    return _lib().linear_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code == LINEAR_OK:
+        return
+    if code in (LINEAR_E_DEVICE, LINEAR_E_LAUNCH):
+        raise LinearError(code, what)
+    raise LinearArgumentError(code, what)
+
+
+def _mat(t: torch.Tensor, name: str):
+    if t.dtype != torch.float16:
+        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit inner stride" % name)
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0), 1)
+    return t.data_ptr(), ld
+
+
+def _stream_handle(stream, *tensors):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _prepare(x, weight, b, out):
+    xp, ldx = _mat(x, "x")
+    wp, ldw = _mat(weight, "weight")
+    M, K = x.shape
+    N, K2 = weight.shape
+    if K != K2:
+        raise ValueError("x is [%d, %d] but weight is [%d, %d]" % (M, K, N, K2))
+    bp = None
+    if b is not None:
+        if b.dtype != torch.float16 or b.dim() != 1 or b.shape[0] != N or (N > 1 and b.stride(0) != 1):
+            raise ValueError("b must be a contiguous float16 [N] tensor")
+        bp = b.data_ptr()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    yp, ldy = _mat(out, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [%d, %d]" % (M, N))
+    return xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K
+
+
+def linear_f16(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """y = FP16(FP16(x @ weight.T) + b) on the GPU (x [M,K], weight [N,K], b [N], float16)."""
+    if b is None:
+        raise ValueError("linear_f16 needs a bias; use linear_f16_nobias")
+    xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out)
+    rc = _lib().linear_f16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    _check(rc, "linear_f16")
+    return out
+
+
+def linear_f16_nobias(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """proj = FP16(x @ weight.T) on the GPU."""
+    xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out)
+    rc = _lib().linear_f16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    _check(rc, "linear_f16_nobias")
+    return out
+
+
+def linear_f16_ex(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None,
+                  out: torch.Tensor | None = None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """linear_f16 with a forced path (PATH_AUTO / PATH_GEMM / PATH_SKINNY) and optional bias."""
+    xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out)
+    rc = _lib().linear_f16_ex(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, int(path),
+                              _stream_handle(stream, x, out))
+    _check(rc, "linear_f16_ex")
+    return out
+
+
+def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, path: int = PATH_AUTO) -> dict:
+    """The kernel and tile a call would use (host only)."""
+    if out is None:
+        out = torch.empty((x.shape[0], weight.shape[0]), dtype=torch.float16, device="meta")
+        yp, ldy = 0x100000000, max(weight.shape[0], 1)
+    else:
+        yp, ldy = _mat(out, "out")
+    xp, ldx = _mat(x, "x")
+    wp, ldw = _mat(weight, "weight")
+    p = _Plan()
+    rc = _lib().linear_f16_plan(xp, ldx, wp, ldw, None if b is None else b.data_ptr(), yp, ldy,
+                                x.shape[0], weight.shape[0], x.shape[1], int(path), ctypes.byref(p))
+    _check(rc, "linear_f16_plan")
+    return {f: getattr(p, f) for f, _ in _Plan._fields_}
+
+
+def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """Convenience: the bias call when a bias is given, the projection alone otherwise."""
+    if bias is None:
+        return linear_f16_nobias(x, weight, out=out)
+    return linear_f16(x, weight, bias, out=out)

@@ -1,0 +1,250 @@
+// linear_abi.hip -- the C ABI: argument validation, path and tile choice, launch.
+//
+// All shape, stride, alias and path checks run on the host before anything is
+// enqueued, and kernel choice is a host decision made from the static shapes
+// (as the poot Graph IR pages do it: shapes are inferred on the host and GEMV
+// versus GEMM is chosen when the call is planned, not inside a kernel).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/linear_amd.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxLdIn = (int64_t(1) << 22) - 1;
+constexpr int64_t kMaxLdOut = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxGridX = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxGridY = 65535;
+constexpr int kSkinnyMaxM = 16;   // AUTO sends M <= 16 to the skinny path
+constexpr int kNumCUs = 256;
+
+struct Extent {
+    uintptr_t lo, hi;  // [lo, hi) in bytes; hi == lo when empty
+};
+
+Extent extent(const void* p, int64_t rows, int64_t ld, int64_t cols) {
+    Extent e{(uintptr_t)p, (uintptr_t)p};
+    if (p && rows > 0 && cols > 0) e.hi = e.lo + (uintptr_t)(((rows - 1) * ld + cols) * 2);
+    return e;
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+struct Request {
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* w;
+    int64_t ldw;
+    const uint16_t* b;
+    uint16_t* y;
+    int64_t ldy;
+    int64_t M, N, K;
+    int32_t path;
+    bool need_bias;  // the bias entry point: b must be present
+};
+
+// Shape, pointer, stride, alias and path checks.  Pure host logic.
+int32_t validate(const Request& r) {
+    if (r.M < 0 || r.N < 0 || r.K < 0) return LINEAR_E_SHAPE;
+    if (r.M > kMaxDim || r.N > kMaxDim || r.K > kMaxDim) return LINEAR_E_SHAPE;
+    if (r.path != LINEAR_PATH_AUTO && r.path != LINEAR_PATH_GEMM && r.path != LINEAR_PATH_SKINNY)
+        return LINEAR_E_PATH;
+    if (r.M == 0 || r.N == 0) return LINEAR_OK;  // nothing to write
+    if (!r.y) return LINEAR_E_NULL;
+    if (r.K > 0 && (!r.x || !r.w)) return LINEAR_E_NULL;
+    if (r.need_bias && !r.b) return LINEAR_E_NULL;
+    if (r.ldx < r.K || r.ldw < r.K || r.ldy < r.N) return LINEAR_E_STRIDE;
+    if (r.ldx > kMaxLdIn || r.ldw > kMaxLdIn || r.ldy > kMaxLdOut) return LINEAR_E_STRIDE;
+    const Extent ey = extent(r.y, r.M, r.ldy, r.N);
+    if (overlaps(ey, extent(r.x, r.M, r.ldx, r.K))) return LINEAR_E_ALIAS;
+    if (overlaps(ey, extent(r.w, r.N, r.ldw, r.K))) return LINEAR_E_ALIAS;
+    if (r.b && overlaps(ey, extent(r.b, 1, r.N, r.N))) return LINEAR_E_ALIAS;
+    return LINEAR_OK;
+}
+
+bool vector_loads_ok(const Request& r) {
+    return ((uintptr_t)r.x % 16 == 0) && ((uintptr_t)r.w % 16 == 0) && (r.ldx % 8 == 0) &&
+           (r.ldw % 8 == 0) && (r.K % 8 == 0);
+}
+
+bool vector_store_ok(const Request& r) { return ((uintptr_t)r.y % 8 == 0) && (r.ldy % 4 == 0); }
+
+// Relative throughput of one workgroup of each GEMM configuration while it runs
+// alone on a CU (larger tiles reuse each loaded byte for more MFMAs), in units of
+// the 256x256 tile's rate.  Used to trade tile efficiency against wave
+// quantization on the 256 CUs.
+const double kCfgRate[lin::kNumGemmConfigs] = {1.00, 0.92, 0.92, 0.80, 0.45};
+
+int choose_gemm_config(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    int best = 0;
+    double best_t = 1e300;
+    for (int c = 0; c < lin::kNumGemmConfigs; ++c) {
+        const lin::GemmConfig& g = lin::kGemmConfigs[c];
+        const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+        if (tiles > kMaxGridX / 64) continue;
+        const int64_t waves = (tiles + kNumCUs - 1) / kNumCUs;
+        const double t = (double)waves * (double)g.bm * (double)g.bn / kCfgRate[c];
+        if (t < best_t * 0.999) {
+            best_t = t;
+            best = c;
+        }
+    }
+    return best;
+}
+
+int32_t plan(const Request& r, linear_plan* p) {
+    memset(p, 0, sizeof *p);
+    int32_t path = r.path;
+    if (path == LINEAR_PATH_AUTO) path = (r.M <= kSkinnyMaxM) ? LINEAR_PATH_SKINNY : LINEAR_PATH_GEMM;
+    p->path = path;
+    p->vector_io = vector_loads_ok(r) ? 1 : 0;
+    if (path == LINEAR_PATH_SKINNY) {
+        p->tile_m = lin::kSkinnyTile;
+        p->tile_n = lin::kSkinnyTile;
+        p->tile_k = lin::kSkinnyKStep;
+        p->threads = lin::kSkinnyWaves * 64;
+        const int64_t gx = (r.N + 15) / 16, gy = (r.M + 15) / 16;
+        if (gx > kMaxGridX || gy > kMaxGridY) return LINEAR_E_SHAPE;
+        p->grid = gx * gy;
+    } else {
+        const int c = choose_gemm_config(r.M, r.N, r.K);
+        const lin::GemmConfig& g = lin::kGemmConfigs[c];
+        p->tile_m = g.bm;
+        p->tile_n = g.bn;
+        p->tile_k = 64;
+        p->threads = g.wm * g.wn * 64;
+        p->grid = ((r.M + g.bm - 1) / g.bm) * ((r.N + g.bn - 1) / g.bn);
+        if (p->grid > kMaxGridX / 64) return LINEAR_E_SHAPE;
+    }
+    return LINEAR_OK;
+}
+
+// Device check, cached per device: the current device must be a gfx950.
+int32_t check_device(int* dev_out) {
+    static int cached[64];  // 0 unknown, 1 gfx950, 2 other
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        g_last_hip_error = (int32_t)e;
+        return LINEAR_E_DEVICE;
+    }
+    if (dev < 64 && cached[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int32_t)e;
+            return LINEAR_E_DEVICE;
+        }
+        cached[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (dev >= 64 || cached[dev] != 1) return LINEAR_E_DEVICE;
+    *dev_out = dev;
+    return LINEAR_OK;
+}
+
+int32_t run(const Request& r, void* stream) {
+    int32_t st = validate(r);
+    if (st != LINEAR_OK) return st;
+    if (r.M == 0 || r.N == 0) return LINEAR_OK;
+    linear_plan p;
+    st = plan(r, &p);
+    if (st != LINEAR_OK) return st;
+    int dev = 0;
+    st = check_device(&dev);
+    if (st != LINEAR_OK) return st;
+
+    lin::LinearArgs a;
+    a.x = r.x;
+    a.w = r.w;
+    a.b = r.b;
+    a.y = r.y;
+    a.ldx = r.ldx;
+    a.ldw = r.ldw;
+    a.ldy = r.ldy;
+    a.M = (int)r.M;
+    a.N = (int)r.N;
+    a.K = (int)r.K;
+    a.vec_store = vector_store_ok(r) ? 1 : 0;
+    const bool bias = r.b != nullptr;
+    const bool vec = p.vector_io != 0;
+    hipError_t e;
+    if (p.path == LINEAR_PATH_SKINNY) {
+        a.tiles_m = (int)((r.M + 15) / 16);
+        a.tiles_n = (int)((r.N + 15) / 16);
+        e = lin::launch_skinny(a, vec, bias, (hipStream_t)stream);
+    } else {
+        const int c = choose_gemm_config(r.M, r.N, r.K);
+        const lin::GemmConfig& g = lin::kGemmConfigs[c];
+        a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
+        a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
+        e = lin::launch_gemm(c, a, vec, bias, (hipStream_t)stream);
+    }
+    if (e != hipSuccess) {
+        g_last_hip_error = (int32_t)e;
+        return LINEAR_E_LAUNCH;
+    }
+    return LINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                   const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                   void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, LINEAR_PATH_AUTO, true};
+    return run(r, stream);
+}
+
+int32_t linear_f16_nobias(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                          uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, LINEAR_PATH_AUTO, false};
+    return run(r, stream);
+}
+
+int32_t linear_f16_ex(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                      const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                      int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false};
+    return run(r, stream);
+}
+
+int32_t linear_f16_plan(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                        const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                        int32_t path, linear_plan* out) {
+    if (!out) return LINEAR_E_NULL;
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false};
+    int32_t st = validate(r);
+    if (st != LINEAR_OK) return st;
+    if (M == 0 || N == 0) {
+        memset(out, 0, sizeof *out);
+        out->path = path == LINEAR_PATH_AUTO ? LINEAR_PATH_SKINNY : path;
+        return LINEAR_OK;
+    }
+    return plan(r, out);
+}
+
+const char* linear_status_string(int32_t status) {
+    switch (status) {
+        case LINEAR_OK: return "ok";
+        case LINEAR_E_NULL: return "a required pointer is NULL";
+        case LINEAR_E_SHAPE: return "invalid shape: M, N or K negative or too large";
+        case LINEAR_E_STRIDE: return "invalid row stride: ldx/ldw < K, ldy < N, or beyond the stride limit";
+        case LINEAR_E_ALIAS: return "y overlaps x, weight or b";
+        case LINEAR_E_PATH: return "unknown path selector";
+        case LINEAR_E_DEVICE: return "no usable gfx950 device is current";
+        case LINEAR_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t linear_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

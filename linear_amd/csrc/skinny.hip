@@ -1,0 +1,110 @@
+// skinny.hip -- the small-M (decode) path of the FP16 linear layer on gfx950.
+//
+// For M <= 16 the layer is a weight stream: every weight element is used by at
+// most 16 rows of x, so the time is the time to read weight[N, K] once from HBM.
+// One workgroup owns 16 weight rows (16 output columns n) and up to 16 rows of x;
+// its waves split K into contiguous ranges, so all of the block's weight bytes
+// are in flight at once.  Each wave contracts its range with
+// v_mfma_f32_16x16x32_f16 (weight rows as the A operand, x rows as B; rows of x
+// past M read as zero through the buffer resource, costing no memory traffic),
+// keeping FP32 partial sums in registers.  The partial tiles are then added in
+// FP32 through LDS in a fixed wave order (deterministic), and only that full-K
+// sum is rounded to FP16, followed by the bias epilogue ("tensor programs, part
+// 1", section "One Program and One Numerical Contract").
+//
+// Within one MFMA step of 32 K values, lane l supplies weight row (l % 16) and
+// x row (l % 16) over the same 8 K values, chunk 4u + l/16 of the row: the four
+// lanes of one row read 64 contiguous bytes, and A and B always pair the same K.
+#include "common.h"
+#include "kernels.h"
+
+namespace lin {
+
+template <int WAVES, bool VEC, bool BIAS>
+__global__ void __launch_bounds__(WAVES * 64)
+skinny_f16_kernel(LinearArgs a) {
+    constexpr int UNROLL = 8;
+    const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    const int K = a.K;
+
+    const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n0, a.N, a.ldw, K);
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, m0, a.M, a.ldx, K);
+    const uint32_t wrow = (uint32_t)((int64_t)row * a.ldw * 2);
+    const uint32_t xrow = (uint32_t)((int64_t)row * a.ldx * 2);
+    const bool w_ok = n0 + row < a.N, x_ok = m0 + row < a.M;
+
+    const int U = (K + 31) / 32;
+    const int ub = (int)((int64_t)wave * U / WAVES);
+    const int ue = (int)((int64_t)(wave + 1) * U / WAVES);
+
+    f32x4 acc = (f32x4){};
+    for (int u = ub; u < ue; u += UNROLL) {
+        u32x4 wa[UNROLL], xb[UNROLL];
+#pragma unroll
+        for (int s = 0; s < UNROLL; ++s) {
+            const int k = ((u + s) * 4 + grp) * 8;   // first K of this lane's chunk
+            const bool in = (u + s) < ue;
+            if (VEC) {
+                const bool kin = in && k < K;
+                wa[s] = load16(rw, (kin && w_ok) ? wrow + 2u * (uint32_t)k : kOOB);
+                xb[s] = load16(rx, (kin && x_ok) ? xrow + 2u * (uint32_t)k : kOOB);
+            } else {
+                wa[s] = load8_masked(rw, wrow + 2u * (uint32_t)k, k, in ? K : 0, w_ok);
+                xb[s] = load8_masked(rx, xrow + 2u * (uint32_t)k, k, in ? K : 0, x_ok);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < UNROLL; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wa[s]), as_f16x8(xb[s]), acc, 0, 0, 0);
+    }
+
+    __shared__ f32x4 red[WAVES][64];
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) s += red[w][lane];
+
+    // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
+    const int m = m0 + (lane & 15);
+    const int nb = n0 + (lane >> 4) * 4;
+    if (m >= a.M) return;
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (BIAS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
+    }
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(s[e], bias[e]);
+    uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
+    if (a.vec_store && nb + 3 < a.N) {
+        uint2 v;
+        v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *(uint2*)dst = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) dst[e] = o[e];
+    }
+}
+
+hipError_t launch_skinny(const LinearArgs& a, bool vec, bool bias, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
+    const dim3 block(kSkinnyWaves * 64);
+    LinearArgs args = a;
+    void* params[] = {&args};
+    const void* fn;
+    if (vec) fn = bias ? (const void*)skinny_f16_kernel<kSkinnyWaves, true, true>
+                       : (const void*)skinny_f16_kernel<kSkinnyWaves, true, false>;
+    else fn = bias ? (const void*)skinny_f16_kernel<kSkinnyWaves, false, true>
+                   : (const void*)skinny_f16_kernel<kSkinnyWaves, false, false>;
+    return hipLaunchKernel(fn, grid, block, params, 0, stream);
+}
+
+}  // namespace lin

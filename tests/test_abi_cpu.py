@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: exported symbols, host-side validation, plans."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+import linear_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linear_amd.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(la.LIB_PATH), reason="liblinear_amd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(linear_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == set(la.ENTRY_POINTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(la._lib(), name)
+
+
+@needs_lib
+def test_status_strings():
+    for code in range(0, 8):
+        assert la.linear_status_string(code)
+    assert la.linear_status_string(99) == "unknown status"
+
+
+# Fake device addresses: validation must reject these calls before touching memory.
+X = 0x7F0000000000
+W = 0x7F1000000000
+B = 0x7F2000000000
+Y = 0x7F3000000000
+
+
+def call(x=X, ldx=64, w=W, ldw=64, b=B, y=Y, ldy=32, M=8, N=32, K=64, path=0):
+    return la._lib().linear_f16_ex(x, ldx, w, ldw, b, y, ldy, M, N, K, path, None)
+
+
+def call_bias(x=X, ldx=64, w=W, ldw=64, b=B, y=Y, ldy=32, M=8, N=32, K=64):
+    return la._lib().linear_f16(x, ldx, w, ldw, b, y, ldy, M, N, K, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), la.LINEAR_E_SHAPE),
+    (dict(N=-5), la.LINEAR_E_SHAPE),
+    (dict(K=-1), la.LINEAR_E_SHAPE),
+    (dict(M=1 << 31), la.LINEAR_E_SHAPE),
+    (dict(x=0), la.LINEAR_E_NULL),
+    (dict(w=0), la.LINEAR_E_NULL),
+    (dict(y=0), la.LINEAR_E_NULL),
+    (dict(ldx=63), la.LINEAR_E_STRIDE),
+    (dict(ldw=10), la.LINEAR_E_STRIDE),
+    (dict(ldy=31), la.LINEAR_E_STRIDE),
+    (dict(ldx=1 << 22, ldw=64), la.LINEAR_E_STRIDE),
+    (dict(path=3), la.LINEAR_E_PATH),
+    (dict(path=-1), la.LINEAR_E_PATH),
+    (dict(y=X + 100), la.LINEAR_E_ALIAS),           # y starts inside x
+    (dict(y=W - 10), la.LINEAR_E_ALIAS),            # y runs into w
+    (dict(b=Y + 2 * 32 * 3), la.LINEAR_E_ALIAS),    # b inside y
+])
+def test_validation_errors_are_reported_before_any_device_work(kw, code):
+    assert call(**kw) == code
+
+
+@needs_lib
+def test_bias_entry_point_requires_bias():
+    assert call_bias(b=0) == la.LINEAR_E_NULL
+
+
+@needs_lib
+def test_empty_output_is_a_noop_even_with_null_pointers():
+    assert call(x=0, w=0, b=0, y=0, M=0) == la.LINEAR_OK
+    assert call(x=0, w=0, b=0, y=0, N=0) == la.LINEAR_OK
+
+
+@needs_lib
+def test_k0_allows_null_inputs_until_the_device_check():
+    # K == 0: x and w are never read, so NULL is accepted; without a GPU the call then
+    # stops at the device check.
+    rc = call(x=0, w=0, K=0, ldx=0, ldw=0)
+    assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
+    if not torch.cuda.is_available():
+        assert rc == la.LINEAR_E_DEVICE
+
+
+@needs_lib
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_a_device_reports_device_error():
+    assert call() == la.LINEAR_E_DEVICE
+    assert la._lib().linear_last_hip_error() != 0
+
+
+def plan(M, N, K, path=0, x=X, w=W, ldx=None, ldw=None):
+    p = la._Plan()
+    rc = la._lib().linear_f16_plan(x, ldx or K, w, ldw or K, B, Y, N, M, N, K, path, ctypes.byref(p))
+    assert rc == la.LINEAR_OK
+    return {f: getattr(p, f) for f, _ in la._Plan._fields_}
+
+
+@needs_lib
+def test_plans_for_the_workloads():
+    from linear_amd.workloads import WORKLOADS
+    for name, wl in WORKLOADS.items():
+        p = plan(wl.M, wl.N, wl.K)
+        if wl.M <= 16:
+            assert p["path"] == la.PATH_SKINNY, name
+        else:
+            assert p["path"] == la.PATH_GEMM, name
+            assert p["grid"] >= 256 or name == "toy", (name, p)
+        assert p["vector_io"] == 1
+
+
+@needs_lib
+def test_plan_falls_back_to_elementwise_loader():
+    assert plan(64, 64, 63)["vector_io"] == 0          # K % 8 != 0
+    assert plan(64, 64, 64, x=X + 2)["vector_io"] == 0  # misaligned x
+    assert plan(64, 64, 64, ldx=72)["vector_io"] == 1   # padded stride, still aligned
+    assert plan(64, 64, 64, ldw=66)["vector_io"] == 0
+
+
+@needs_lib
+def test_forced_paths():
+    assert plan(1000, 64, 64, path=la.PATH_SKINNY)["path"] == la.PATH_SKINNY
+    assert plan(1, 64, 64, path=la.PATH_GEMM)["path"] == la.PATH_GEMM
+
+
+def test_product_package_does_not_import_the_oracle():
+    for root, _, files in os.walk(os.path.join(ROOT, "linear_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle.c" not in text and "liboracle" not in text, f

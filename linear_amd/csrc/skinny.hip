@@ -15,10 +15,108 @@
 // Within one MFMA step of 32 K values, lane l supplies weight row (l % 16) and
 // x row (l % 16) over the same 8 K values, chunk 4u + l/16 of the row: the four
 // lanes of one row read 64 contiguous bytes, and A and B always pair the same K.
+//
+// Two variants:
+//  - skinny_f16_stream (16-byte aligned layouts): per pass of up to 16 MFMA steps
+//    a wave first copies the rows of x it needs straight into its own LDS region
+//    (one contiguous 1 KB direct-to-LDS load per x row, so at M = 1 a single
+//    instruction instead of one per step), then issues all of its weight loads
+//    back to back (a scheduling barrier keeps the compiler from interleaving them
+//    with the MFMAs, so every load is in flight at once), and consumes each weight
+//    fragment as it arrives.
+//  - skinny_f16_kernel (any layout): element-wise masked loads of both operands.
 #include "common.h"
 #include "kernels.h"
 
 namespace lin {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int WAVES, bool BIAS>
+__global__ void __launch_bounds__(WAVES * 64)
+skinny_f16_stream(LinearArgs a) {
+    constexpr int PU = 16;                    // MFMA steps (32 K values each) per pass
+    constexpr int XPITCH = PU * 64 + 16;      // bytes per LDS row of x: 512 halves + pad
+    __shared__ __attribute__((aligned(16))) unsigned char xs[WAVES * 16 * XPITCH];
+    __shared__ f32x4 red[WAVES][64];
+
+    const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    const int K = a.K;
+    const int mv = min(16, a.M - m0);         // valid x rows in this block
+
+    const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n0, a.N, a.ldw, K);
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, m0, a.M, a.ldx, K);
+    const uint32_t wrow = (uint32_t)((int64_t)row * a.ldw * 2);
+    unsigned char* xreg = xs + wave * 16 * XPITCH;
+
+    const int U = (K + 31) / 32;
+    const int ub = (int)((int64_t)wave * U / WAVES);
+    const int ue = (int)((int64_t)(wave + 1) * U / WAVES);
+    const int kend = min(ue * 32, K);
+
+    f32x4 acc = (f32x4){};
+    for (int u0 = ub; u0 < ue; u0 += PU) {
+        // x rows j < mv: halves [32 u0 + 8 lane, +8) of each row, zero past kend
+        const int kx = u0 * 32 + lane * 8;
+        for (int j = 0; j < mv; ++j) {
+            const uint32_t off = kx < kend ? (uint32_t)(((int64_t)j * a.ldx + kx) * 2) : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xreg + j * XPITCH), 16, off, 0, 0, 0);
+        }
+        u32x4 wa[PU];
+#pragma unroll
+        for (int s = 0; s < PU; ++s) {
+            const int k = ((u0 + s) * 4 + grp) * 8;
+            wa[s] = load16(rw, k < kend ? wrow + 2u * (uint32_t)k : kOOB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the x copies were issued before the PU weight loads: wait for them alone
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PU) : "memory");
+#pragma unroll
+        for (int s = 0; s < PU; ++s) {
+            const int k = ((u0 + s) * 4 + grp) * 8;
+            // rows past M and K past the range contribute zero (masked, not branched)
+            const uint32_t keep = (row < mv && k < kend) ? 0xffffffffu : 0u;
+            u32x4 xv = *(const u32x4*)(xreg + row * XPITCH + (s * 4 + grp) * 16);
+            xv &= (u32x4){keep, keep, keep, keep};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wa[s]), as_f16x8(xv), acc, 0, 0, 0);
+        }
+        // every LDS read of this pass has been consumed by an MFMA above, so the
+        // next pass may overwrite the region
+    }
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) s += red[w][lane];
+
+    const int m = m0 + (lane & 15);
+    const int nb = n0 + (lane >> 4) * 4;
+    if (m >= a.M) return;
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (BIAS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
+    }
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(s[e], bias[e]);
+    uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
+    if (a.vec_store && nb + 3 < a.N) {
+        uint2 v;
+        v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *(uint2*)dst = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) dst[e] = o[e];
+    }
+}
 
 template <int WAVES, bool VEC, bool BIAS>
 __global__ void __launch_bounds__(WAVES * 64)
@@ -100,8 +198,8 @@ hipError_t launch_skinny(const LinearArgs& a, bool vec, bool bias, hipStream_t s
     LinearArgs args = a;
     void* params[] = {&args};
     const void* fn;
-    if (vec) fn = bias ? (const void*)skinny_f16_kernel<kSkinnyWaves, true, true>
-                       : (const void*)skinny_f16_kernel<kSkinnyWaves, true, false>;
+    if (vec) fn = bias ? (const void*)skinny_f16_stream<kSkinnyWaves, true>
+                       : (const void*)skinny_f16_stream<kSkinnyWaves, false>;
     else fn = bias ? (const void*)skinny_f16_kernel<kSkinnyWaves, false, true>
                    : (const void*)skinny_f16_kernel<kSkinnyWaves, false, false>;
     return hipLaunchKernel(fn, grid, block, params, 0, stream);

@@ -30,6 +30,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPYCAL_BYTES = (64 << 20) * 4   # one copy in --only copycal: 64 Mi float32 read and written
+# sources whose change invalidates recorded counter readings, per kernel
+KERNEL_SOURCES = {
+    "skinny_f16_stream": ["linear_amd/csrc/skinny.hip", "linear_amd/csrc/common.h"],
+    "gemm_f16_stream": ["linear_amd/csrc/gemm.hip", "linear_amd/csrc/common.h"],
+}
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense FP16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 ROTATE_BYTES = 512 * 1024 * 1024
 
@@ -47,7 +54,79 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
+    ap.add_argument("--record-traffic", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR"),
+                    help="store HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE CSV runs")
     return ap.parse_args()
+
+
+def sources_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(csv_dir: str, counter: str):
+    """Mean per-dispatch value of `counter` for each kernel in a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+def record_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                   commands: list[str]):
+    """Turn FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of `kernel` and of the plain
+    copy calibration into bytes per launch, and store them with a hash of the kernel
+    sources so that a later change of the kernel invalidates them."""
+    def pick(d, counter, name):
+        m = _counter_means(d, counter)
+        hits = [(k, v) for k, v in m.items() if name in k]
+        if not hits:
+            raise SystemExit("no %s dispatches of %s under %s" % (counter, name, d))
+        return hits[0]
+    kname, (fetch_kib, nf) = pick(fetch_dir, "FETCH_SIZE", kernel)
+    _, (write_kib, nw) = pick(write_dir, "WRITE_SIZE", kernel)
+    _, (cf_kib, _) = pick(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    _, (cw_kib, _) = pick(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f_scale = COPYCAL_BYTES / (cf_kib * 1024.0)
+    w_scale = COPYCAL_BYTES / (cw_kib * 1024.0)
+    rec = {}
+    if os.path.exists(TRAFFIC_JSON):
+        rec = json.load(open(TRAFFIC_JSON))
+    rec[kernel] = {
+        "kernel_name": kname,
+        "fetch_kib_per_dispatch": round(fetch_kib, 1),
+        "write_kib_per_dispatch": round(write_kib, 1),
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": COPYCAL_BYTES, "fetch_kib": round(cf_kib, 1), "write_kib": round(cw_kib, 1),
+                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "bytes_per_launch": round(fetch_kib * 1024.0 * f_scale + write_kib * 1024.0 * w_scale),
+        "sources_sha": sources_hash(kernel),
+        "commands": commands,
+    }
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec[kernel]))
+
+
+def recorded_traffic(kernel: str):
+    """Bytes per launch from the counter runs, or None if absent or the kernel changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_JSON))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha") != sources_hash(kernel):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def rotation_sets(bytes_per_set: int) -> int:
@@ -184,6 +263,17 @@ def cpu_baseline(workloads, target_s: float = 10.0):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        k, fd, wd, cfd, cwd = args.record_traffic
+        record_traffic(k, fd, wd, cfd, cwd, [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py --only decode "
+            "--steps 16 --warmup 8 --repeats 1",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -- python3 bench.py --only decode "
+            "--steps 16 --warmup 8 --repeats 1",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <COPY_FETCH_DIR> -- python3 bench.py --only copycal",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <COPY_WRITE_DIR> -- python3 bench.py --only copycal",
+        ])
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -200,7 +290,16 @@ def main():
     log("device:", torch.cuda.get_device_name(0))
 
     if args.only:
-        if args.only == "decode":
+        if args.only == "copycal":
+            # a plain device-to-device copy of known size: the reference that scales the
+            # FETCH_SIZE / WRITE_SIZE counters to bytes
+            src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copycal: 5 copies of %d bytes" % (src.numel() * 4))
+        elif args.only == "decode":
             ms, _ = bench_decode(args, torch, la, workloads, stream)
             log("decode ms/step %.5f" % ms)
         else:
@@ -249,7 +348,8 @@ def main():
                         "W [4096,4096], b [4096], fp16",
             "calls_per_step": launches,
             "weight_copies_rotated": detail["weight_copies"],
-            "kernel": "skinny_f16_kernel (16x16 tile, 8 waves, v_mfma_f32_16x16x32_f16)",
+            "kernel": "skinny_f16_stream (16 output columns x 16 rows per workgroup, 8 waves, "
+                      "v_mfma_f32_16x16x32_f16)",
         },
         "roofline": {
             "bound": "hbm",
@@ -257,8 +357,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "skinny_f16_kernel",
+            "traffic": recorded_traffic("skinny_f16_stream"),
+            "kernel": "skinny_f16_stream",
             "bytes_per_launch": per_launch_bytes,
             "us_per_launch": round(per_launch_s * 1e6, 3),
         },

@@ -46,6 +46,16 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS load: each lane's 16 bytes at byte offset `off` of the resource
+// land at lds + 16 * lane (lds must be the same for the whole wave).  Out-of-range
+// offsets deliver zeros.  Kept out of lambdas: inside one, the host compilation
+// pass drops the enclosing kernel's launch stub.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
 // Eight consecutive binary16 elements starting at byte offset `off`, element e
 // replaced by zero when k0 + e >= K (element-wise loader for unaligned layouts).
 __device__ inline u32x4 load8_masked(__amdgpu_buffer_rsrc_t r, uint32_t off, int k0, int K, bool row_ok) {

@@ -18,8 +18,10 @@
 //    slice t+1 are issued before the MFMAs of slice t, written to the other LDS
 //    buffer after them, one barrier per slice.
 //  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ (r & 7) so that the ds_read_b128 of 8 consecutive rows at one K offset
-//    touches 8 different bank groups.
+//    c ^ ((r >> 1) & 7).  The LDS serves a 16-byte-per-lane read 16 lanes (256
+//    bytes) at a time, so the 16 consecutive rows one such group reads at one K
+//    offset must fall in 16 different 16-byte bank groups: two rows share each
+//    256-byte span and the XOR separates the rest.
 //  - Ragged M, N and K need no special tiles: loads go through buffer
 //    resources whose range ends at the matrix's last valid element, so rows past
 //    M or N and K chunks past K read as zero; stores are masked.
@@ -58,7 +60,7 @@ gemm_f16_kernel(LinearArgs a) {
     constexpr int CW = BN / RSTEP, CX = BM / RSTEP;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(CW * RSTEP == BN && CX * RSTEP == BM, "tile rows must be a multiple of NT/8");
-    static_assert(RSTEP % 8 == 0, "swizzle assumes rows of one thread share r & 7");
+    static_assert(RSTEP % 16 == 0, "swizzle assumes rows of one thread share (r >> 1) & 7");
     constexpr int STAGE = (BN + BM) * BK;       // halves per LDS stage
     __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
@@ -73,7 +75,7 @@ gemm_f16_kernel(LinearArgs a) {
     const int tid = threadIdx.x;
     const int kc = tid & 7;          // this thread's 16-byte chunk within a BK slice
     const int r0 = tid >> 3;         // first tile row it loads; then r0 + i * RSTEP
-    const int swz = (kc ^ (r0 & 7)) << 3;
+    const int swz = (kc ^ ((r0 >> 1) & 7)) << 3;
 
     uint32_t woff[CW], xoff[CX];
 #pragma unroll
@@ -130,7 +132,7 @@ gemm_f16_kernel(LinearArgs a) {
         const f16* sx = sw + BN * BK;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ((ks * 2 + lh) ^ (lr & 7)) << 3;
+            const int ch = ((ks * 2 + lh) ^ ((lr >> 1) & 7)) << 3;
             f16x8 av[FN], bv[FM];
 #pragma unroll
             for (int i = 0; i < FN; ++i) av[i] = *(const f16x8*)(sw + (wn * TN + i * 32 + lr) * BK + ch);
@@ -183,6 +185,216 @@ gemm_f16_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming variant for 16-byte aligned layouts (x, weight 16-byte aligned, ldx,
+// ldw and K multiples of 8).
+//
+// K-slices of BK (32 or 64) move from HBM straight into LDS with direct-to-LDS
+// buffer loads (no register staging, no LDS write instructions), through a ring
+// of STAGES slots: slice t + STAGES is requested as soon as slot t is retired, so
+// each load has STAGES - 1 slices of MFMA work to arrive in.
+//
+// The fragment reads are software pipelined by hand: the fragments of the next
+// K step are read while the MFMAs of the current one run, and the one barrier
+// per slice sits between the last fragment reads of slice t and its last MFMAs,
+// so the barrier, the next request and the first reads of slice t + 1 overlap
+// MFMA work already queued.  Scheduling-group barriers pin that order.
+//
+// LDS layout of a slice: tile rows of 2 BK bytes (CPR = BK / 8 chunks of 8
+// halves), chunk c of row r stored at chunk c ^ ((r / RP) % CPR), RP = 256 / (2 BK)
+// rows per 256-byte span.  The LDS serves 16 lanes (256 bytes) of a 16-byte read
+// per cycle; an MFMA fragment read (32 consecutive rows, one logical chunk) then
+// touches 16 distinct 16-byte bank groups in each group of 16 lanes.  A direct
+// load fills 1 KB = 1024 / (2 BK) consecutive rows; lane l lands at byte 16 l,
+// i.e. row l / CPR, stored chunk l % CPR, so it fetches the logical chunk that the
+// swizzle puts there.  With BK = 64 every load instruction covers whole 128-byte
+// rows.
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, bool BIAS>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_f16_stream(LinearArgs a) {
+    constexpr int KS = BK / 16;                       // MFMA K steps per slice
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWB = BK * 2;                      // bytes per LDS tile row
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+    constexpr int RP = 256 / ROWB;                    // rows per 256-byte span
+    constexpr int RPL = 1024 / ROWB;                  // rows per direct load
+    constexpr int SLICE = (BN + BM) * ROWB;           // bytes per slot (weight rows first)
+    constexpr int GROUPS = (BN + BM) / RPL;           // direct loads per slice
+    constexpr int GPW = GROUPS / NW;                  // loads per wave per slice
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(GROUPS % NW == 0, "row groups must divide evenly over the waves");
+    static_assert(BN % RPL == 0, "weight rows must fill whole direct loads");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(STAGES >= 2 && STAGES * SLICE <= 160 * 1024, "LDS ring too large");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = a.K;
+    const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n0, a.N, a.ldw, K);
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, m0, a.M, a.ldx, K);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+
+    // This wave's loads: groups g = wave * GPW + j; group g < BN / RPL holds weight
+    // rows RPL g .., the others x rows.  Lane l fetches row l / CPR of the group,
+    // logical chunk (l % CPR) ^ ((row / RP) % CPR).
+    uint32_t goff[GPW];
+    int gk[GPW];                                   // first K element this lane fetches
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int g = wave * GPW + j;
+        const bool isw = g < BN / RPL;
+        const int tr = g * RPL + lane / CPR;       // row within the slot (weight rows first)
+        const int r = isw ? tr : tr - BN;          // row within its matrix tile
+        const int c = (lane % CPR) ^ ((tr / RP) % CPR);
+        gk[j] = c * 8;
+        goff[j] = (uint32_t)(((int64_t)r * (isw ? a.ldw : a.ldx) + c * 8) * 2);
+    }
+
+    const int nk = (K + BK - 1) / BK;
+#define LIN_ISSUE(t_)                                                                    \
+    do {                                                                                 \
+        const int t__ = (t_);                                                            \
+        unsigned char* slot__ = smem + (t__ % STAGES) * SLICE;                           \
+        const uint32_t kb__ = (uint32_t)(t__ * BK) * 2u;                                 \
+        _Pragma("unroll") for (int j = 0; j < GPW; ++j) {                                \
+            const int g = wave * GPW + j;                                                \
+            const bool kin__ = t__ * BK + gk[j] < K;                                     \
+            lds_dma16(g < BN / RPL ? rw : rx, slot__ + g * 1024, kin__ ? goff[j] + kb__ : kOOB); \
+        }                                                                                \
+    } while (0)
+
+    const int wn = wave % WN, wm = wave / WN;
+    const int lr = lane & 31, lh = lane >> 5;
+    // byte offsets of this lane's fragment rows within a slot, per K step
+    uint32_t aoff[KS][FN], boff[KS][FM];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int r = wn * TN + i * 32 + lr;
+            aoff[ks][i] = r * ROWB + (((ks * 2 + lh) ^ ((r / RP) % CPR)) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int r = BN + wm * TM + j * 32 + lr;
+            boff[ks][j] = r * ROWB + (((ks * 2 + lh) ^ ((r / RP) % CPR)) << 4);
+        }
+    }
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
+
+    if (nk > 0) {
+        // Requests past the last slice carry out-of-range offsets (zero fill, no
+        // memory traffic), so exactly STAGES - 1 slices are always in flight
+        // behind the one being waited for and every wait below is static.
+#pragma unroll
+        for (int t = 0; t < STAGES; ++t) LIN_ISSUE(t);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 1) * GPW) : "memory");
+        __syncthreads();
+
+        f16x8 af[2][FN], bf[2][FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) af[0][i] = *(const f16x8*)(smem + aoff[0][i]);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) bf[0][j] = *(const f16x8*)(smem + boff[0][j]);
+
+        auto read_frags = [&](const unsigned char* slot, int ks, int buf) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) af[buf][i] = *(const f16x8*)(slot + aoff[ks][i]);
+#pragma unroll
+            for (int j = 0; j < FM; ++j) bf[buf][j] = *(const f16x8*)(slot + boff[ks][j]);
+        };
+        auto mfmas = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+        };
+        // K steps 0 .. KS-2 of a slice: read the next step while this one multiplies
+        auto inner_steps = [&](const unsigned char* slot) {
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ++ks) {
+                read_frags(slot, ks + 1, (ks + 1) & 1);
+                mfmas(ks & 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        for (int t = 0; t + 1 < nk; ++t) {
+            const unsigned char* cur = smem + (t % STAGES) * SLICE;
+            inner_steps(cur);
+            // slice t + 1 has landed once only the STAGES - 2 later requests are
+            // outstanding; the barrier also waits for every wave's last reads of
+            // slot t, which the refill below overwrites
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
+            __syncthreads();
+            LIN_ISSUE(t + STAGES);
+            read_frags(smem + ((t + 1) % STAGES) * SLICE, 0, KS & 1);
+            mfmas((KS - 1) & 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+#pragma unroll
+            for (int j = 0; j < GPW; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - GPW, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        inner_steps(smem + ((nk - 1) % STAGES) * SLICE);
+        mfmas((KS - 1) & 1);
+        // the zero-fill requests past the end must land before the LDS is released
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#undef LIN_ISSUE
+
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int nb = n0 + wn * TN + i * 32 + g * 8 + lh * 4;
+            float bias[4] = {0.f, 0.f, 0.f, 0.f};
+            if (BIAS) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
+            }
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wm * TM + j * 32 + lr;
+                if (m >= a.M) continue;
+                uint16_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(acc[i][j][g * 4 + e], bias[e]);
+                uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
+                if (a.vec_store && nb + 3 < a.N) {
+                    uint2 v;
+                    v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                    v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                    *(uint2*)dst = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (nb + e < a.N) dst[e] = o[e];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers: one per tile configuration.
 
 template <int BM, int BN, int WM, int WN>
@@ -200,12 +412,12 @@ static hipError_t launch_cfg(const LinearArgs& a, bool vec, bool bias, hipStream
 }
 
 const GemmConfig kGemmConfigs[kNumGemmConfigs] = {
-    // BM, BN, WM, WN
-    {256, 256, 2, 2},
-    {256, 128, 2, 2},
-    {128, 256, 2, 2},
-    {128, 128, 2, 2},
-    {64, 64, 2, 2},
+    // BM, BN, WM, WN, stages, BK
+    {256, 256, 2, 2, 2, 64},
+    {256, 128, 2, 2, 2, 64},
+    {128, 256, 2, 2, 2, 64},
+    {128, 128, 2, 2, 2, 64},
+    {64, 64, 2, 2, 2, 64},
 };
 
 hipError_t launch_gemm(int cfg, const LinearArgs& a, bool vec, bool bias, hipStream_t stream) {
@@ -215,6 +427,47 @@ hipError_t launch_gemm(int cfg, const LinearArgs& a, bool vec, bool bias, hipStr
         case 2: return launch_cfg<128, 256, 2, 2>(a, vec, bias, stream);
         case 3: return launch_cfg<128, 128, 2, 2>(a, vec, bias, stream);
         case 4: return launch_cfg<64, 64, 2, 2>(a, vec, bias, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
+static hipError_t launch_stream_cfg(const LinearArgs& a, bool bias, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+    const dim3 block(WM * WN * 64);
+    LinearArgs args = a;
+    void* params[] = {&args};
+    const void* fn = bias ? (const void*)gemm_f16_stream<BM, BN, WM, WN, STAGES, BK, true>
+                          : (const void*)gemm_f16_stream<BM, BN, WM, WN, STAGES, BK, false>;
+    return hipLaunchKernel(fn, grid, block, params, 0, stream);
+}
+
+const GemmConfig kStreamConfigs[kNumStreamConfigs] = {
+    // BM, BN, WM, WN, stages, BK
+    {256, 256, 2, 4, 4, 32},
+    {256, 256, 2, 4, 2, 64},
+    {256, 256, 2, 2, 2, 64},
+    {256, 128, 4, 2, 4, 32},
+    {256, 128, 4, 2, 3, 64},
+    {128, 256, 2, 4, 4, 32},
+    {128, 128, 2, 2, 4, 32},
+    {64, 64, 2, 2, 4, 32},
+    {128, 128, 2, 2, 4, 64},
+    {64, 64, 2, 2, 4, 64},
+};
+
+hipError_t launch_gemm_stream(int cfg, const LinearArgs& a, bool bias, hipStream_t stream) {
+    switch (cfg) {
+        case 0: return launch_stream_cfg<256, 256, 2, 4, 4, 32>(a, bias, stream);
+        case 1: return launch_stream_cfg<256, 256, 2, 4, 2, 64>(a, bias, stream);
+        case 2: return launch_stream_cfg<256, 256, 2, 2, 2, 64>(a, bias, stream);
+        case 3: return launch_stream_cfg<256, 128, 4, 2, 4, 32>(a, bias, stream);
+        case 4: return launch_stream_cfg<256, 128, 4, 2, 3, 64>(a, bias, stream);
+        case 5: return launch_stream_cfg<128, 256, 2, 4, 4, 32>(a, bias, stream);
+        case 6: return launch_stream_cfg<128, 128, 2, 2, 4, 32>(a, bias, stream);
+        case 7: return launch_stream_cfg<64, 64, 2, 2, 4, 32>(a, bias, stream);
+        case 8: return launch_stream_cfg<128, 128, 2, 2, 4, 64>(a, bias, stream);
+        case 9: return launch_stream_cfg<64, 64, 2, 2, 4, 64>(a, bias, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -74,10 +74,9 @@ bool vector_loads_ok(const Request& r) {
 
 bool vector_store_ok(const Request& r) { return ((uintptr_t)r.y % 8 == 0) && (r.ldy % 4 == 0); }
 
-// Relative throughput of one workgroup of each GEMM configuration while it runs
-// alone on a CU (larger tiles reuse each loaded byte for more MFMAs), in units of
-// the 256x256 tile's rate.  Used to trade tile efficiency against wave
-// quantization on the 256 CUs.
+// Tile choice for the register-staged kernel (unaligned layouts): trade tile
+// efficiency (relative rate of one workgroup, larger tiles reuse each loaded
+// byte for more MFMAs) against wave quantization on the 256 CUs.
 const double kCfgRate[lin::kNumGemmConfigs] = {1.00, 0.92, 0.92, 0.80, 0.45};
 
 int choose_gemm_config(int64_t M, int64_t N, int64_t K) {
@@ -98,6 +97,34 @@ int choose_gemm_config(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
+// Tile choice for the streaming kernel (aligned layouts).  Measured on MI355X, a
+// 256x256 tile sustains the highest rate, and a partial last wave of large tiles
+// costs little, so: the largest tile that still gives every CU at least one tile;
+// when no tile size does, the one that keeps the most CUs busy at its rate.
+struct StreamChoice {
+    int cfg;
+    double rate;   // sustained throughput relative to the 256x256 tile
+};
+// configurations 1, 4, 5, 8, 9 of kStreamConfigs: 256x256, 256x128, 128x256, 128x128, 64x64
+const StreamChoice kStreamOrder[] = {{1, 1.00}, {4, 0.94}, {5, 0.85}, {8, 0.80}, {9, 0.57}};
+
+int choose_stream_config(int64_t M, int64_t N) {
+    int best = 9;
+    double best_score = -1.0;
+    for (const StreamChoice& c : kStreamOrder) {
+        const lin::GemmConfig& g = lin::kStreamConfigs[c.cfg];
+        const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+        if (tiles > kMaxGridX / 64) continue;
+        if (tiles >= kNumCUs) return c.cfg;
+        const double score = (double)tiles * c.rate;
+        if (score > best_score) {
+            best_score = score;
+            best = c.cfg;
+        }
+    }
+    return best;
+}
+
 int32_t plan(const Request& r, linear_plan* p) {
     memset(p, 0, sizeof *p);
     int32_t path = r.path;
@@ -113,11 +140,12 @@ int32_t plan(const Request& r, linear_plan* p) {
         if (gx > kMaxGridX || gy > kMaxGridY) return LINEAR_E_SHAPE;
         p->grid = gx * gy;
     } else {
-        const int c = choose_gemm_config(r.M, r.N, r.K);
-        const lin::GemmConfig& g = lin::kGemmConfigs[c];
+        const bool stream = p->vector_io != 0;
+        const int c = stream ? choose_stream_config(r.M, r.N) : choose_gemm_config(r.M, r.N, r.K);
+        const lin::GemmConfig& g = stream ? lin::kStreamConfigs[c] : lin::kGemmConfigs[c];
         p->tile_m = g.bm;
         p->tile_n = g.bn;
-        p->tile_k = 64;
+        p->tile_k = g.bk;
         p->threads = g.wm * g.wn * 64;
         p->grid = ((r.M + g.bm - 1) / g.bm) * ((r.N + g.bn - 1) / g.bn);
         if (p->grid > kMaxGridX / 64) return LINEAR_E_SHAPE;
@@ -178,6 +206,12 @@ int32_t run(const Request& r, void* stream) {
         a.tiles_m = (int)((r.M + 15) / 16);
         a.tiles_n = (int)((r.N + 15) / 16);
         e = lin::launch_skinny(a, vec, bias, (hipStream_t)stream);
+    } else if (vec) {
+        const int c = choose_stream_config(r.M, r.N);
+        const lin::GemmConfig& g = lin::kStreamConfigs[c];
+        a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
+        a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
+        e = lin::launch_gemm_stream(c, a, bias, (hipStream_t)stream);
     } else {
         const int c = choose_gemm_config(r.M, r.N, r.K);
         const lin::GemmConfig& g = lin::kGemmConfigs[c];

@@ -30,8 +30,6 @@
 
 namespace lin {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int WAVES, bool BIAS>
 __global__ void __launch_bounds__(WAVES * 64)
 skinny_f16_stream(LinearArgs a) {
@@ -62,7 +60,7 @@ skinny_f16_stream(LinearArgs a) {
         const int kx = u0 * 32 + lane * 8;
         for (int j = 0; j < mv; ++j) {
             const uint32_t off = kx < kend ? (uint32_t)(((int64_t)j * a.ldx + kx) * 2) : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xreg + j * XPITCH), 16, off, 0, 0, 0);
+            lds_dma16(rx, xreg + j * XPITCH, off);
         }
         u32x4 wa[PU];
 #pragma unroll

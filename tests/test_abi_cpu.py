@@ -149,3 +149,12 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+@needs_lib
+def test_every_kernel_launch_stub_is_defined():
+    """Each kernel the library launches must be defined in the library itself (the
+    host compilation pass can silently drop a kernel's launch stub)."""
+    out = subprocess.run(["nm", "-C", la.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "lin::" in l]
+    assert not undefined, undefined[:5]

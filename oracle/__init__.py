@@ -66,6 +66,21 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_linear_f16_points.argtypes = [_u16p, _i64, _u16p, _i64, _u16p, _i64, _i64p, _i64p,
                                              _i64, _u16p, _u16p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_linear_f16_points.restype = None
+    lib.oracle_linear.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _u16p, _u16p, _u16p, _f32p, _i64,
+                                  _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_linear.restype = ctypes.c_int
+    lib.oracle_linear_points.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _u16p, _i64, _i64p, _i64p,
+                                         _i64, _u16p, _u16p, _f32p, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_linear_points.restype = None
+    lib.oracle_band.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _i64, _i64, _i64, _f64p, _f64p,
+                                ctypes.c_int]
+    lib.oracle_band.restype = ctypes.c_int
+    lib.oracle_bf16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
+    lib.oracle_bf16_to_f32_array.restype = None
+    lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
+    lib.oracle_f32_to_bf16_array.restype = None
+    lib.oracle_bias_epilogue_elem_array.argtypes = [ctypes.c_int, _u16p, _u16p, _u16p, _i64]
+    lib.oracle_bias_epilogue_elem_array.restype = None
     lib.oracle_band_f64.argtypes = [_u16p, _i64, _u16p, _i64, _i64, _i64, _i64, _f64p, _f64p,
                                     ctypes.c_int]
     lib.oracle_band_f64.restype = ctypes.c_int
@@ -92,8 +107,12 @@ def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+F16 = 0
+BF16 = 1
+
+
 def _as_words(a) -> np.ndarray:
-    """Accept a numpy float16/uint16 array or a CPU torch float16 tensor; return uint16 words."""
+    """Accept a numpy float16/uint16 array or a CPU torch float16/bfloat16 tensor; return uint16 words."""
     if hasattr(a, "detach"):  # torch tensor, CPU
         a = a.detach().contiguous().view(dtype=__import__("torch").int16).numpy().view(np.uint16)
     a = np.asarray(a)
@@ -123,18 +142,36 @@ class Oracle:
         self.lib.oracle_f32_to_f16_array(_ptr(f, ctypes.c_float), _ptr(out, ctypes.c_uint16), f.size)
         return out
 
-    def bias_epilogue(self, proj16, b16) -> np.ndarray:
+    def bf16_to_f32(self, h) -> np.ndarray:
+        h = _as_words(h)
+        out = np.empty(h.shape, np.float32)
+        self.lib.oracle_bf16_to_f32_array(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+        return out
+
+    def f32_to_bf16(self, f) -> np.ndarray:
+        f = np.ascontiguousarray(np.asarray(f, dtype=np.float32))
+        out = np.empty(f.shape, np.uint16)
+        self.lib.oracle_f32_to_bf16_array(_ptr(f, ctypes.c_float), _ptr(out, ctypes.c_uint16), f.size)
+        return out
+
+    def bias_epilogue(self, proj16, b16, elem: int = F16) -> np.ndarray:
         p = _as_words(proj16)
         b = _as_words(b16)
         assert p.shape == b.shape
         out = np.empty(p.shape, np.uint16)
-        self.lib.oracle_bias_epilogue_array(_ptr(p, ctypes.c_uint16), _ptr(b, ctypes.c_uint16),
-                                            _ptr(out, ctypes.c_uint16), p.size)
+        if elem == F16:
+            self.lib.oracle_bias_epilogue_array(_ptr(p, ctypes.c_uint16), _ptr(b, ctypes.c_uint16),
+                                                _ptr(out, ctypes.c_uint16), p.size)
+        else:
+            self.lib.oracle_bias_epilogue_elem_array(elem, _ptr(p, ctypes.c_uint16), _ptr(b, ctypes.c_uint16),
+                                                     _ptr(out, ctypes.c_uint16), p.size)
         return out
 
     # -- the layer ---------------------------------------------------------------
-    def linear(self, x, w, b=None, nthreads: int = 0):
-        """Return (y, proj) as uint16 [M,N] arrays.  x: [M,K], w: [N,K], b: [N] or None."""
+    def linear(self, x, w, b=None, nthreads: int = 0, elem: int = F16, sums: bool = False):
+        """Return (y, proj) as uint16 [M,N] arrays (and the unrounded FP32 sums as a
+        third float32 array if sums).  x: [M,K], w: [N,K], b: [N] or None.
+        elem: F16 (binary16) or BF16 (bfloat16) operand and output words."""
         x = _as_words(x)
         w = _as_words(w)
         M, K = x.shape
@@ -145,19 +182,21 @@ class Oracle:
             assert bb.shape == (N,)
         y = np.zeros((M, N), np.uint16)
         proj = np.zeros((M, N), np.uint16)
-        rc = self.lib.oracle_linear_f16(
-            _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16), max(K, 1),
+        y32 = np.zeros((M, N), np.float32) if sums else None
+        rc = self.lib.oracle_linear(
+            int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16), max(K, 1),
             None if bb is None else _ptr(bb, ctypes.c_uint16),
-            _ptr(y, ctypes.c_uint16), _ptr(proj, ctypes.c_uint16), max(N, 1), M, N, K, nthreads)
+            _ptr(y, ctypes.c_uint16), _ptr(proj, ctypes.c_uint16),
+            None if y32 is None else _ptr(y32, ctypes.c_float), max(N, 1), M, N, K, nthreads)
         if rc != 0:
-            raise MemoryError("oracle_linear_f16 failed")
-        return y, proj
+            raise MemoryError("oracle_linear failed")
+        return (y, proj, y32) if sums else (y, proj)
 
-    def points(self, x, w, b, ms, ns, nthreads: int = 0):
+    def points(self, x, w, b, ms, ns, nthreads: int = 0, elem: int = F16):
         """Evaluate the definition at coordinates (ms[i], ns[i]).
 
-        Returns dict(y, proj, S, A): uint16 y and proj, float64 S = sum x*w and
-        A = sum |x*w| (FP64, products exact)."""
+        Returns dict(y, proj, y32, S, A): uint16 y and proj, float32 unrounded sums
+        y32, float64 S = sum x*w and A = sum |x*w| (FP64, products exact)."""
         x = _as_words(x)
         w = _as_words(w)
         ms = np.ascontiguousarray(ms, dtype=np.int64)
@@ -167,17 +206,18 @@ class Oracle:
         bb = None if b is None else _as_words(b)
         y = np.zeros(count, np.uint16)
         proj = np.zeros(count, np.uint16)
+        y32 = np.zeros(count, np.float32)
         S = np.zeros(count, np.float64)
         A = np.zeros(count, np.float64)
-        self.lib.oracle_linear_f16_points(
-            _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16), max(K, 1),
+        self.lib.oracle_linear_points(
+            int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16), max(K, 1),
             None if bb is None else _ptr(bb, ctypes.c_uint16), K,
             _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64), count,
-            _ptr(y, ctypes.c_uint16), _ptr(proj, ctypes.c_uint16),
+            _ptr(y, ctypes.c_uint16), _ptr(proj, ctypes.c_uint16), _ptr(y32, ctypes.c_float),
             _ptr(S, ctypes.c_double), _ptr(A, ctypes.c_double), nthreads)
-        return {"y": y, "proj": proj, "S": S, "A": A}
+        return {"y": y, "proj": proj, "y32": y32, "S": S, "A": A}
 
-    def band(self, x, w, nthreads: int = 0):
+    def band(self, x, w, nthreads: int = 0, elem: int = F16):
         """FP64 S = x @ w.T and A = |x| @ |w|.T for the whole output (small problems)."""
         x = _as_words(x)
         w = _as_words(w)
@@ -185,9 +225,9 @@ class Oracle:
         N = w.shape[0]
         S = np.zeros((M, N), np.float64)
         A = np.zeros((M, N), np.float64)
-        rc = self.lib.oracle_band_f64(_ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16),
-                                      max(K, 1), M, N, K, _ptr(S, ctypes.c_double),
-                                      _ptr(A, ctypes.c_double), nthreads)
+        rc = self.lib.oracle_band(int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16),
+                                  max(K, 1), M, N, K, _ptr(S, ctypes.c_double),
+                                  _ptr(A, ctypes.c_double), nthreads)
         if rc != 0:
             raise MemoryError("oracle_band_f64 failed")
         return S, A

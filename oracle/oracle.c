@@ -20,6 +20,11 @@
  * from the IEEE 754 binary16 / binary32 encodings, not taken from a compiler
  * intrinsic or a library.
  *
+ * The same definition with bfloat16 operands ("The Graph IR", op table: a Cast
+ * to bf16 rounds to bf16 precision; ContractionEpilogue: a BF16 head rounds to
+ * BF16 before the first epilogue step reads it) and the unrounded FP32 sum (the op
+ * table's DenseContraction produces f32) are provided too.
+ *
  * Readings where the pages are silent (all listed in the design notes):
  *   - "rounded to FP16" is IEEE roundTiesToEven, with gradual underflow
  *     (subnormals kept) and overflow to infinity;
@@ -130,6 +135,40 @@ uint16_t oracle_f32_to_f16(float f) {
     return (uint16_t)(sign | (uint16_t)q);
 }
 
+/* ---------------------------------------------------------------------------
+ * bfloat16: by definition the upper 16 bits of a binary32 (1 sign, 8 exponent,
+ * 7 fraction bits), so widening places the word in the upper half (exact), and
+ * rounding keeps the upper half, rounded to nearest, ties to even, on the
+ * discarded lower 16 bits.  A NaN stays a (quiet) NaN; rounding up past the
+ * largest finite value carries into the exponent and gives infinity, as IEEE
+ * rounding does.
+ * ------------------------------------------------------------------------- */
+float oracle_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u = bits_from_f32(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);                    /* quiet NaN */
+    uint32_t q = u >> 16;
+    uint32_t rem = u & 0xffffu;
+    if (rem > 0x8000u || (rem == 0x8000u && (q & 1u))) q += 1u;   /* may carry into the exponent */
+    return (uint16_t)q;
+}
+
+/* Element-type dispatch: 0 = binary16, 1 = bfloat16. */
+static float widen16(int elem, uint16_t h) { return elem ? oracle_bf16_to_f32(h) : oracle_f16_to_f32(h); }
+static uint16_t narrow16(int elem, float f) { return elem ? oracle_f32_to_bf16(f) : oracle_f32_to_f16(f); }
+
+void oracle_bf16_to_f32_array(const uint16_t* h, float* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f32(h[i]);
+}
+
+void oracle_f32_to_bf16_array(const float* f, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(f[i]);
+}
+
 void oracle_f16_to_f32_array(const uint16_t* h, float* out, int64_t n) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f32(h[i]);
@@ -152,6 +191,16 @@ void oracle_bias_epilogue_array(const uint16_t* p, const uint16_t* b, uint16_t* 
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_bias_epilogue(p[i], b[i]);
 }
 
+/* The bias epilogue for either element type. */
+static uint16_t bias_epilogue16(int elem, uint16_t proj16, uint16_t b16) {
+    return narrow16(elem, widen16(elem, proj16) + widen16(elem, b16));
+}
+
+void oracle_bias_epilogue_elem_array(int elem, const uint16_t* p, const uint16_t* b, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = bias_epilogue16(elem, p[i], b[i]);
+}
+
 /* The FP32 accumulation for one output element: sequential k order from +0.
    Each product of two binary16 values is exact in binary32 (11 + 11 significand
    bits, exponents within range), so only the additions round. */
@@ -163,12 +212,12 @@ static float dot_f32(const float* xr, const float* wr, int64_t K) {
 
 /* Widen a row-major [rows, cols] binary16 matrix with row stride ld to a dense
    FP32 copy (test-side only; the GPU path never widens). */
-static float* widen(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols) {
+static float* widen(int elem, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols) {
     float* dst = (float*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(cols > 0 ? cols : 1) * sizeof(float));
     if (!dst) return NULL;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c) dst[r * cols + c] = oracle_f16_to_f32(src[r * ld + c]);
+        for (int64_t c = 0; c < cols; ++c) dst[r * cols + c] = widen16(elem, src[r * ld + c]);
     return dst;
 }
 
@@ -176,33 +225,41 @@ static float* widen(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols)
  * Full oracle.  x: [M,K] row stride ldx; w: [N,K] row stride ldw (the
  * [out_features, in_features] weight, contracted over its second axis, i.e. the
  * transposed weight is a view); b: [N] or NULL; outputs y and proj: [M,N] row
- * stride ldy (either may be NULL).  With b == NULL, y = proj.
+ * stride ldy (either may be NULL).  With b == NULL, y = proj.  elem: 0 binary16,
+ * 1 bfloat16.  y32 (may be NULL): the unrounded FP32 sums, row stride ldy.
  * nthreads <= 0 uses the OpenMP default.  Returns 0, or -1 on allocation failure.
  */
-int oracle_linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
-                      const uint16_t* b, uint16_t* y, uint16_t* proj, int64_t ldy,
-                      int64_t M, int64_t N, int64_t K, int nthreads) {
+int oracle_linear(int elem, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                  const uint16_t* b, uint16_t* y, uint16_t* proj, float* y32, int64_t ldy,
+                  int64_t M, int64_t N, int64_t K, int nthreads) {
     if (M <= 0 || N <= 0) return 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
     (void)nthreads;
 #endif
-    float* xf = widen(x, ldx, M, K);
-    float* wf = widen(w, ldw, N, K);
+    float* xf = widen(elem, x, ldx, M, K);
+    float* wf = widen(elem, w, ldw, N, K);
     if (!xf || !wf) { free(xf); free(wf); return -1; }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             float acc = dot_f32(xf + m * K, wf + n * K, K);
-            uint16_t p16 = oracle_f32_to_f16(acc);
+            if (y32) y32[m * ldy + n] = acc;
+            uint16_t p16 = narrow16(elem, acc);
             if (proj) proj[m * ldy + n] = p16;
-            if (y) y[m * ldy + n] = b ? oracle_bias_epilogue(p16, b[n]) : p16;
+            if (y) y[m * ldy + n] = b ? bias_epilogue16(elem, p16, b[n]) : p16;
         }
     }
     free(xf);
     free(wf);
     return 0;
+}
+
+int oracle_linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                      const uint16_t* b, uint16_t* y, uint16_t* proj, int64_t ldy,
+                      int64_t M, int64_t N, int64_t K, int nthreads) {
+    return oracle_linear(0, x, ldx, w, ldw, b, y, proj, NULL, ldy, M, N, K, nthreads);
 }
 
 /*
@@ -211,10 +268,10 @@ int oracle_linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t
  * the outputs may be NULL.  S and A are the FP64 band data: S = sum_k x*w and
  * A = sum_k |x*w|, each product exact in FP64 (used by the tolerance rule).
  */
-void oracle_linear_f16_points(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
-                              const uint16_t* b, int64_t K, const int64_t* ms, const int64_t* ns,
-                              int64_t count, uint16_t* y_out, uint16_t* proj_out,
-                              double* S_out, double* A_out, int nthreads) {
+void oracle_linear_points(int elem, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                          const uint16_t* b, int64_t K, const int64_t* ms, const int64_t* ns,
+                          int64_t count, uint16_t* y_out, uint16_t* proj_out, float* y32_out,
+                          double* S_out, double* A_out, int nthreads) {
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -227,32 +284,40 @@ void oracle_linear_f16_points(const uint16_t* x, int64_t ldx, const uint16_t* w,
         float acc = 0.0f;
         double S = 0.0, A = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            float xv = oracle_f16_to_f32(xr[k]);
-            float wv = oracle_f16_to_f32(wr[k]);
+            float xv = widen16(elem, xr[k]);
+            float wv = widen16(elem, wr[k]);
             acc = acc + xv * wv;
             double pd = (double)xv * (double)wv;
             S += pd;
             A += fabs(pd);
         }
-        uint16_t p16 = oracle_f32_to_f16(acc);
+        uint16_t p16 = narrow16(elem, acc);
         if (proj_out) proj_out[i] = p16;
-        if (y_out) y_out[i] = b ? oracle_bias_epilogue(p16, b[ns[i]]) : p16;
+        if (y_out) y_out[i] = b ? bias_epilogue16(elem, p16, b[ns[i]]) : p16;
+        if (y32_out) y32_out[i] = acc;
         if (S_out) S_out[i] = S;
         if (A_out) A_out[i] = A;
     }
 }
 
+void oracle_linear_f16_points(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                              const uint16_t* b, int64_t K, const int64_t* ms, const int64_t* ns,
+                              int64_t count, uint16_t* y_out, uint16_t* proj_out,
+                              double* S_out, double* A_out, int nthreads) {
+    oracle_linear_points(0, x, ldx, w, ldw, b, K, ms, ns, count, y_out, proj_out, NULL, S_out, A_out, nthreads);
+}
+
 /* FP64 band data for a whole [M,N] output (small problems only). */
-int oracle_band_f64(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
-                    int64_t M, int64_t N, int64_t K, double* S, double* A, int nthreads) {
+int oracle_band(int elem, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                int64_t M, int64_t N, int64_t K, double* S, double* A, int nthreads) {
     if (M <= 0 || N <= 0) return 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
     (void)nthreads;
 #endif
-    float* xf = widen(x, ldx, M, K);
-    float* wf = widen(w, ldw, N, K);
+    float* xf = widen(elem, x, ldx, M, K);
+    float* wf = widen(elem, w, ldw, N, K);
     if (!xf || !wf) { free(xf); free(wf); return -1; }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; ++m) {
@@ -270,6 +335,11 @@ int oracle_band_f64(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t l
     free(xf);
     free(wf);
     return 0;
+}
+
+int oracle_band_f64(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                    int64_t M, int64_t N, int64_t K, double* S, double* A, int nthreads) {
+    return oracle_band(0, x, ldx, w, ldw, M, N, K, S, A, nthreads);
 }
 
 int oracle_max_threads(void) {

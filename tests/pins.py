@@ -379,9 +379,148 @@ def pin_toy_shapes():
     assert wl.K == spec["contraction_K"]
 
 
+# --------------------------------------------------------------------------- bfloat16
+
+def rne_bf16_ref(d) -> np.ndarray:
+    """Round FP64 values to bfloat16 (8 significant bits), ties to even, via frexp/rint;
+    returns the bfloat16 words.  Valid for results in the normal range."""
+    d = np.asarray(d, np.float64)
+    m, e = np.frexp(d)
+    r = np.ldexp(np.rint(m * 256.0), e - 8)        # numpy rint rounds half to even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_words_to_f64(h) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16(vals) -> np.ndarray:
+    return rne_bf16_ref(np.asarray(vals, np.float64))
+
+
+def pin_bf16_decode_exhaustive(orc):
+    """bfloat16 -> binary32 for all 65,536 words vs torch's conversion."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.bf16_to_f32(h)
+    want = torch.from_numpy(h.astype(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def check_bf16_rne_words(orc, words: np.ndarray):
+    f = words.view(np.float32)
+    got = orc.f32_to_bf16(f)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    gf = got.view(np.uint16)
+    nan_g = (gf & 0x7F80) == 0x7F80
+    nan_g &= (gf & 0x007F) != 0
+    nan_w = ((want & 0x7F80) == 0x7F80) & ((want & 0x007F) != 0)
+    ok = (got == want) | (nan_g & nan_w)
+    if not ok.all():
+        i = np.flatnonzero(~ok)[:5]
+        raise AssertionError("f32->bf16: %d mismatches, e.g. %s -> %s want %s" % (
+            (~ok).sum(), words[i].tolist(), got[i].tolist(), want[i].tolist()))
+
+
+def pin_bf16_rne_sampled(orc, count: int = 1 << 22, seed: int = 21):
+    """binary32 -> bfloat16 on random words plus every exponent with the low 17 bits
+    enumerated (tie, carry and overflow patterns), vs torch's conversion."""
+    g = np.random.default_rng(seed)
+    rnd = g.integers(0, 1 << 32, count, dtype=np.uint64).astype(np.uint32)
+    exps = np.arange(256, dtype=np.uint32) << 23
+    low = np.arange(1 << 17, dtype=np.uint32)
+    highs = np.array([0, 0x7E0000, 0x520000], np.uint32)
+    grid = (exps[:, None, None] | highs[None, :, None] | low[None, None, :]).ravel()
+    check_bf16_rne_words(orc, np.concatenate([rnd, grid, grid | np.uint32(0x80000000)]))
+
+
+def _random_bf16(shape, seed, lo=-20, hi=20):
+    """Random finite bfloat16 words with exponents in [lo, hi] (results stay normal)."""
+    g = np.random.default_rng(seed)
+    e = g.integers(lo, hi + 1, shape)
+    m = g.integers(0, 128, shape)
+    sgn = g.integers(0, 2, shape)
+    v = np.ldexp(1.0 + m / 128.0, e) * np.where(sgn == 1, -1.0, 1.0)
+    return rne_bf16_ref(v)
+
+
+def pin_bf16_epilogue_vs_exact(orc, count: int = 1 << 20, seed: int = 22):
+    """RNE_bf16(f32(p) + f32(b)) equals the FP64 sum rounded once to bfloat16."""
+    p = _random_bf16(count, seed)
+    b = _random_bf16(count, seed + 1)
+    got = orc.bias_epilogue(p, b, elem=1)
+    exact = bf16_words_to_f64(p) + bf16_words_to_f64(b)
+    want = rne_bf16_ref(exact)
+    zero = exact == 0
+    want[zero] = 0
+    ok = (got == want) | (zero & ((got & 0x7FFF) == 0))
+    assert ok.all(), int((~ok).sum())
+
+
+def pin_bf16_k1_closed_form(orc, count: int = 1 << 15, seed: int = 23):
+    """K = 1 in bfloat16: proj = RNE_bf16(x * w), the product exact in FP64."""
+    x = _random_bf16((count, 1), seed)
+    w = _random_bf16((count, 1), seed + 1)
+    ms = np.arange(count)
+    r = orc.points(x, w, None, ms, ms, elem=1)
+    want = rne_bf16_ref(bf16_words_to_f64(x[:, 0]) * bf16_words_to_f64(w[:, 0]))
+    assert np.array_equal(r["proj"], want)
+
+
+def pin_bf16_small_integers(orc, seed: int = 24):
+    """Integer bfloat16 inputs: every order is exact; proj is the integer sum rounded once."""
+    for (M, N, K) in ((17, 23, 300), (5, 9, 1), (40, 3, 700)):
+        x, w, b = workloads.small_integers(M, N, K, seed=seed + K)
+        xb, wb, bb = x.to(torch.bfloat16), w.to(torch.bfloat16), b.to(torch.bfloat16)
+        s = x.to(torch.int64).numpy() @ w.to(torch.int64).numpy().T
+        want_p = rne_bf16_ref(s.astype(np.float64))
+        want_y = rne_bf16_ref(bf16_words_to_f64(want_p) + b.to(torch.float64).numpy()[None, :])
+        z = (want_p & 0x7FFF) == 0
+        y, p = orc.linear(xb, wb, bb, elem=1)
+        assert np.array_equal(p[~z], want_p[~z]) and ((p[z] & 0x7FFF) == 0).all(), "bf16 int proj"
+        zy = (want_y & 0x7FFF) == 0
+        assert np.array_equal(y[~zy], want_y[~zy]) and ((y[zy] & 0x7FFF) == 0).all(), "bf16 int y"
+
+
+def pin_bf16_golden_round_before_bias(orc):
+    """The hand-derived cases of tests/golden/round_before_bias_bf16.txt."""
+    for line in open(os.path.join(GOLDEN, "round_before_bias_bf16.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        xs, ws, b, p, y, _ = [t.strip() for t in line.split(";")]
+        x = _bf16([[float(v) for v in xs.split(",")]])
+        w = _bf16([[float(v) for v in ws.split(",")]])
+        bb = _bf16([float(b)])
+        assert bf16_words_to_f64(x).ravel().tolist() == [float(t) for t in xs.split(",")], xs
+        yy, pp = orc.linear(x, w, bb, elem=1)
+        assert bf16_words_to_f64(pp)[0, 0] == float(p), (line, bf16_words_to_f64(pp))
+        assert bf16_words_to_f64(yy)[0, 0] == float(y), (line, bf16_words_to_f64(yy))
+
+
+def pin_f32_sums(orc, seed: int = 25):
+    """The unrounded sums: equal to a numpy float32 left-to-right accumulation, and
+    within the recursive-summation bound of the FP64 sum."""
+    for elem, dt in ((0, torch.float16), (1, torch.bfloat16)):
+        x, w, _ = workloads.make_inputs(7, 11, 37, 0.2, seed=seed + elem)
+        x, w = x.to(dt), w.to(dt)
+        _, _, y32 = orc.linear(x, w, None, elem=elem, sums=True)
+        xf, wf = x.to(torch.float32).numpy(), w.to(torch.float32).numpy()
+        acc = np.zeros((7, 11), np.float32)
+        for k in range(37):
+            acc = (acc + xf[:, k:k + 1] * wf[None, :, k].reshape(1, 11)).astype(np.float32)
+        assert np.array_equal(y32, acc), "FP32 sums differ from the left-to-right float32 loop"
+        S = x.to(torch.float64).numpy() @ w.to(torch.float64).numpy().T
+        A = np.abs(x.to(torch.float64).numpy()) @ np.abs(w.to(torch.float64).numpy()).T
+        gamma = 36 * 2.0 ** -24 / (1 - 36 * 2.0 ** -24)
+        assert (np.abs(y32 - S) <= gamma * A + 1e-30).all()
+
+
 FAST_PINS = [
     pin_decode_exhaustive, pin_rne_spot_values, pin_rne_sampled, pin_bias_epilogue_vs_exact,
     pin_k1_closed_form, pin_k2_unique, pin_small_k_trees, pin_identity, pin_one_hot,
     pin_small_integers, pin_golden_round_before_bias, pin_k0_empty_sum, pin_scale_invariance,
     pin_permutations, pin_thread_determinism, pin_random_band, pin_strided_layout,
+    pin_bf16_decode_exhaustive, pin_bf16_rne_sampled, pin_bf16_epilogue_vs_exact, pin_bf16_k1_closed_form,
+    pin_bf16_small_integers, pin_bf16_golden_round_before_bias, pin_f32_sums,
 ]

@@ -21,10 +21,10 @@ MUTANTS = [
      "if (rem > half && 0) q += 1u;"),
     ("ties_away_from_zero", "if (rem > half || (rem == half && (q & 1u))) q += 1u;",
      "if (rem >= half) q += 1u;"),
-    ("bias_before_rounding", "if (y) y[m * ldy + n] = b ? oracle_bias_epilogue(p16, b[n]) : p16;",
-     "if (y) y[m * ldy + n] = b ? oracle_f32_to_f16(acc + oracle_f16_to_f32(b[n])) : p16;"),
-    ("bias_wrong_index", "if (y) y[m * ldy + n] = b ? oracle_bias_epilogue(p16, b[n]) : p16;",
-     "if (y) y[m * ldy + n] = b ? oracle_bias_epilogue(p16, b[m % N]) : p16;"),
+    ("bias_before_rounding", "if (y) y[m * ldy + n] = b ? bias_epilogue16(elem, p16, b[n]) : p16;",
+     "if (y) y[m * ldy + n] = b ? narrow16(elem, acc + widen16(elem, b[n])) : p16;"),
+    ("bias_wrong_index", "if (y) y[m * ldy + n] = b ? bias_epilogue16(elem, p16, b[n]) : p16;",
+     "if (y) y[m * ldy + n] = b ? bias_epilogue16(elem, p16, b[m % N]) : p16;"),
     ("flush_subnormal_inputs", "mag = ldexpf((float)frac, -24);", "mag = 0.0f * (float)frac;"),
     ("drop_sign", "return sign ? -mag : mag;", "return mag;"),
     ("product_rounded_to_f16", "acc = acc + xr[k] * wr[k];",
@@ -43,6 +43,15 @@ MUTANTS = [
      "float acc = 1e-6f;\n    for (int64_t k = 0; k < K; ++k) acc = acc + xr[k] * wr[k];"),
     ("points_wrong_stride", "const uint16_t* xr = x + ms[i] * ldx;", "const uint16_t* xr = x + ms[i] * K;"),
     ("band_abs_missing", "                a += fabs(pd);", "                a += pd;"),
+    ("bf16_truncate", "if (rem > 0x8000u || (rem == 0x8000u && (q & 1u))) q += 1u;   /* may carry into the exponent */",
+     "if (rem > 0x8000u && 0) q += 1u;"),
+    ("bf16_ties_away", "if (rem > 0x8000u || (rem == 0x8000u && (q & 1u))) q += 1u;   /* may carry into the exponent */",
+     "if (rem >= 0x8000u) q += 1u;"),
+    ("bf16_decode_shift", "float oracle_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }",
+     "float oracle_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 15); }"),
+    ("bf16_epilogue_as_f16", "return narrow16(elem, widen16(elem, proj16) + widen16(elem, b16));",
+     "return narrow16(elem, widen16(elem, proj16) + widen16(0, b16));"),
+    ("sums_before_accumulate", "if (y32) y32[m * ldy + n] = acc;", "if (y32) y32[m * ldy + n] = acc * 1.0000001f;"),
 ]
 
 

@@ -20,3 +20,11 @@ def test_rne_exhaustive_all_binary32_words(orc):
     for start in range(0, 1 << 32, chunk):
         words = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
         pins.check_rne_words(orc, words)
+
+
+def test_bf16_rne_exhaustive_all_binary32_words(orc):
+    """binary32 -> bfloat16 RNE for all 2^32 words against torch's conversion."""
+    chunk = 1 << 26
+    for start in range(0, 1 << 32, chunk):
+        words = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        pins.check_bf16_rne_words(orc, words)

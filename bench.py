@@ -35,7 +35,8 @@ COPYCAL_BYTES = (64 << 20) * 4   # one copy in --only copycal: 64 Mi float32 rea
 # sources whose change invalidates recorded counter readings, per kernel
 KERNEL_SOURCES = {
     "skinny_f16_stream": ["linear_amd/csrc/skinny.hip", "linear_amd/csrc/common.h"],
-    "gemm_f16_stream": ["linear_amd/csrc/gemm.hip", "linear_amd/csrc/common.h"],
+    "gemm_f16_stream": ["linear_amd/csrc/gemm_impl.h", "linear_amd/csrc/gemm_f16.hip",
+                        "linear_amd/csrc/common.h"],
 }
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense FP16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 ROTATE_BYTES = 512 * 1024 * 1024
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
+    ap.add_argument("--variant", default="f16", help="with --only: f16, bf16, f16_f32out or bf16_f32out")
+    ap.add_argument("--no-variants", action="store_true", help="skip the bfloat16 / FP32-output timings")
     ap.add_argument("--record-traffic", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR"),
                     help="store HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE CSV runs")
@@ -163,20 +166,22 @@ def time_region(graph, replays, stream, torch):
     return start.elapsed_time(end)
 
 
-def bench_decode(args, torch, la, workloads, stream):
+def bench_decode(args, torch, la, workloads, stream, dtype=None):
     """The step: one call at M=1 and one at M=16.  Returns (ms_per_step, detail)."""
+    dtype = dtype or torch.float16
+    fn = la.linear_bf16 if dtype == torch.bfloat16 else la.linear_f16
     w1, w16 = workloads.WORKLOADS["gemv1"], workloads.WORKLOADS["gemv16"]
-    x1, wbase, b = workloads.workload_inputs("gemv1", seed=0, device="cuda")
-    x16, _, _ = workloads.workload_inputs("gemv16", seed=0, device="cuda")
+    x1, wbase, b = workloads.workload_inputs("gemv1", seed=0, device="cuda", dtype=dtype)
+    x16, _, _ = workloads.workload_inputs("gemv16", seed=0, device="cuda", dtype=dtype)
     copies = rotation_sets(wbase.numel() * 2)
     weights = [wbase] + [wbase.clone() for _ in range(copies - 1)]
-    y1 = torch.empty((1, w1.N), dtype=torch.float16, device="cuda")
-    y16 = torch.empty((16, w16.N), dtype=torch.float16, device="cuda")
+    y1 = torch.empty((1, w1.N), dtype=dtype, device="cuda")
+    y16 = torch.empty((16, w16.N), dtype=dtype, device="cuda")
     step_bytes = w1.bytes + w16.bytes
 
     def step(i):
-        la.linear_f16(x1, weights[(2 * i) % copies], b, out=y1, stream=stream)
-        la.linear_f16(x16, weights[(2 * i + 1) % copies], b, out=y16, stream=stream)
+        fn(x1, weights[(2 * i) % copies], b, out=y1, stream=stream)
+        fn(x16, weights[(2 * i + 1) % copies], b, out=y16, stream=stream)
 
     # one graph holds `period` steps, so every weight copy is used once per replay
     period = max(1, copies // 2)
@@ -200,17 +205,31 @@ def bench_decode(args, torch, la, workloads, stream):
     return ms, detail
 
 
-def bench_gemm(name, torch, la, workloads, stream, calls):
+def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
+    """One prefill shape.  variant: "f16" (the layer), "bf16" (bfloat16 layer) or
+    "f16_f32out" / "bf16_f32out" (the unrounded FP32 sums, no bias)."""
     wl = workloads.WORKLOADS[name]
-    x, w, b = workloads.workload_inputs(name, seed=0, device="cuda")
-    sets = rotation_sets(wl.bytes)
+    dtype = torch.bfloat16 if variant.startswith("bf16") else torch.float16
+    sums = variant.endswith("f32out")
+    x, w, b = workloads.workload_inputs(name, seed=0, device="cuda", dtype=dtype)
+    # algorithmic bytes: FP32 output is 4 B per element and there is no bias
+    nbytes = wl.bytes + (2 * wl.M * wl.N - 2 * wl.N if sums else 0)
+    sets = rotation_sets(nbytes)
     xs = [x] + [x.clone() for _ in range(sets - 1)]
     ws = [w] + [w.clone() for _ in range(sets - 1)]
-    ys = [torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda") for _ in range(sets)]
+    ys = [torch.empty((wl.M, wl.N), dtype=torch.float32 if sums else dtype, device="cuda")
+          for _ in range(sets)]
+    if sums:
+        fn = la.linear_bf16_f32out if dtype == torch.bfloat16 else la.linear_f16_f32out
+    else:
+        fn = la.linear_bf16 if dtype == torch.bfloat16 else la.linear_f16
 
     def call(i):
         k = i % sets
-        la.linear_f16(xs[k], ws[k], b, out=ys[k], stream=stream)
+        if sums:
+            fn(xs[k], ws[k], out=ys[k], stream=stream)
+        else:
+            fn(xs[k], ws[k], b, out=ys[k], stream=stream)
 
     graph = capture(call, sets, stream, torch)
     replays = max(1, calls // sets)
@@ -222,11 +241,11 @@ def bench_gemm(name, torch, la, workloads, stream, calls):
     plan = la.linear_f16_plan(x, w, b)
     del xs, ws, ys
     return {
-        "M": wl.M, "N": wl.N, "K": wl.K,
+        "M": wl.M, "N": wl.N, "K": wl.K, "variant": variant,
         "us_per_call": round(ms * 1e3, 3),
         "tflops": round(tflops, 1),
         "frac_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-        "hbm_gbs_algorithmic": round(wl.bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "input_sets": sets,
         "tile": [plan["tile_m"], plan["tile_n"]],
         "grid": plan["grid"],
@@ -300,10 +319,11 @@ def main():
             torch.cuda.synchronize()
             log("copycal: 5 copies of %d bytes" % (src.numel() * 4))
         elif args.only == "decode":
-            ms, _ = bench_decode(args, torch, la, workloads, stream)
+            dt = torch.bfloat16 if args.variant == "bf16" else torch.float16
+            ms, _ = bench_decode(args, torch, la, workloads, stream, dt)
             log("decode ms/step %.5f" % ms)
         else:
-            log(json.dumps(bench_gemm(args.only, torch, la, workloads, stream, 100)))
+            log(json.dumps(bench_gemm(args.only, torch, la, workloads, stream, 100, args.variant)))
         return
 
     log("decode step: %d warmup, %d timed x %d repeats" % (args.warmup, args.steps, args.repeats))
@@ -322,6 +342,19 @@ def main():
             log("prefill", name)
             prefill[name] = bench_gemm(name, torch, la, workloads, stream, calls)
             log(json.dumps(prefill[name]))
+    variants = {}
+    if not args.no_variants:
+        dargs = argparse.Namespace(steps=args.steps, warmup=args.warmup, repeats=args.repeats)
+        dms, _ = bench_decode(dargs, torch, la, workloads, stream, torch.bfloat16)
+        variants["decode_bf16"] = {"us_per_step": round(dms * 1e3, 3),
+                                   "gbs": round(step_bytes / (dms * 1e-3) / 1e9, 1),
+                                   "frac_hbm_peak": round(step_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("decode bf16", json.dumps(variants["decode_bf16"]))
+        if not args.no_prefill:
+            for name, calls, var in (("attn", 50, "bf16"), ("attn", 50, "f16_f32out"),
+                                     ("attn", 50, "bf16_f32out"), ("down", 50, "bf16")):
+                variants["%s_%s" % (name, var)] = r = bench_gemm(name, torch, la, workloads, stream, calls, var)
+                log(json.dumps(r))
     torch.cuda.synchronize()
 
     cpu = None
@@ -364,6 +397,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 

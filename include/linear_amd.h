@@ -95,6 +95,59 @@ int32_t linear_f16_ex(const uint16_t* x, int64_t ldx,
                       int64_t M, int64_t N, int64_t K,
                       int32_t path, void* stream);
 
+/*
+ * The unrounded FP32 sums: y[m,n] = sum_k x[m,k] * weight[n,k] accumulated in FP32
+ * (products exact), stored as float with row stride ldy (elements).  No rounding,
+ * no bias.  This is the op table's DenseContraction with an f32 output ("The
+ * Graph IR", op table) and the rank-local partial product that a K-split tensor
+ * parallel layer all-reduces before rounding and adding the bias ("Model and
+ * Distributed IR", section "Boundary between the layers"; rounding per rank would
+ * break the projection-rounding requirement).  Same conventions otherwise; path
+ * as in linear_f16_ex.  Fast path additionally needs y 16-byte aligned.
+ */
+int32_t linear_f16_f32out(const uint16_t* x, int64_t ldx,
+                          const uint16_t* weight, int64_t ldw,
+                          float* y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K,
+                          int32_t path, void* stream);
+
+/*
+ * The same layer with bfloat16 x, weight, b and y (words are the upper halves of
+ * binary32): FP32 accumulation, the projection rounded to bfloat16 (round to
+ * nearest even) before the bias, then y = BF16(FP32(proj) + FP32(b[n])).  This
+ * is the BF16 form of the contraction epilogue ("The Graph IR", op table:
+ * ContractionEpilogue, a BF16 head rounds to BF16 before the first epilogue step;
+ * Cast to bf16 rounds to bf16 precision).  bfloat16 x bfloat16 products are exact
+ * in FP32 unless they leave its normal range.  Conventions, status codes, paths
+ * and limits as for the binary16 entry points.
+ */
+int32_t linear_bf16(const uint16_t* x, int64_t ldx,
+                    const uint16_t* weight, int64_t ldw,
+                    const uint16_t* b,
+                    uint16_t* y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K,
+                    void* stream);
+
+int32_t linear_bf16_nobias(const uint16_t* x, int64_t ldx,
+                           const uint16_t* weight, int64_t ldw,
+                           uint16_t* y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K,
+                           void* stream);
+
+int32_t linear_bf16_ex(const uint16_t* x, int64_t ldx,
+                       const uint16_t* weight, int64_t ldw,
+                       const uint16_t* b,
+                       uint16_t* y, int64_t ldy,
+                       int64_t M, int64_t N, int64_t K,
+                       int32_t path, void* stream);
+
+/* The unrounded FP32 sums for bfloat16 operands (see linear_f16_f32out). */
+int32_t linear_bf16_f32out(const uint16_t* x, int64_t ldx,
+                           const uint16_t* weight, int64_t ldw,
+                           float* y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K,
+                           int32_t path, void* stream);
+
 /* Which kernel a call would launch.  Pure host function: touches no device. */
 typedef struct linear_plan {
     int32_t path;       /* LINEAR_PATH_GEMM or LINEAR_PATH_SKINNY */

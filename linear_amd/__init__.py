@@ -29,8 +29,9 @@ PATH_AUTO = 0
 PATH_GEMM = 1
 PATH_SKINNY = 2
 
-ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_plan",
-                "linear_status_string", "linear_last_hip_error")
+ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_f32out",
+                "linear_bf16", "linear_bf16_nobias", "linear_bf16_ex", "linear_bf16_f32out",
+                "linear_f16_plan", "linear_status_string", "linear_last_hip_error")
 
 
 class LinearError(RuntimeError):
@@ -71,6 +72,16 @@ def _lib():
     lib.linear_f16_nobias.restype = i32
     lib.linear_f16_ex.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.linear_f16_ex.restype = i32
+    for name in ("linear_bf16",):
+        getattr(lib, name).argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
+        getattr(lib, name).restype = i32
+    lib.linear_bf16_nobias.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.linear_bf16_nobias.restype = i32
+    lib.linear_bf16_ex.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.linear_bf16_ex.restype = i32
+    for name in ("linear_f16_f32out", "linear_bf16_f32out"):
+        getattr(lib, name).argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, vp]
+        getattr(lib, name).restype = i32
     lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
                                     ctypes.POINTER(_Plan)]
     lib.linear_f16_plan.restype = i32
@@ -98,9 +109,9 @@ def _check(code: int, what: str):
     raise LinearArgumentError(code, what)
 
 
-def _mat(t: torch.Tensor, name: str):
-    if t.dtype != torch.float16:
-        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+def _mat(t: torch.Tensor, name: str, dtype=torch.float16):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if t.dim() != 2:
         raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
     if t.shape[1] > 1 and t.stride(1) != 1:
@@ -118,21 +129,22 @@ def _stream_handle(stream, *tensors):
     return ctypes.c_void_p(0)
 
 
-def _prepare(x, weight, b, out):
-    xp, ldx = _mat(x, "x")
-    wp, ldw = _mat(weight, "weight")
+def _prepare(x, weight, b, out, dtype=torch.float16, out_dtype=None):
+    out_dtype = out_dtype or dtype
+    xp, ldx = _mat(x, "x", dtype)
+    wp, ldw = _mat(weight, "weight", dtype)
     M, K = x.shape
     N, K2 = weight.shape
     if K != K2:
         raise ValueError("x is [%d, %d] but weight is [%d, %d]" % (M, K, N, K2))
     bp = None
     if b is not None:
-        if b.dtype != torch.float16 or b.dim() != 1 or b.shape[0] != N or (N > 1 and b.stride(0) != 1):
-            raise ValueError("b must be a contiguous float16 [N] tensor")
+        if b.dtype != dtype or b.dim() != 1 or b.shape[0] != N or (N > 1 and b.stride(0) != 1):
+            raise ValueError("b must be a contiguous %s [N] tensor" % dtype)
         bp = b.data_ptr()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    yp, ldy = _mat(out, "out")
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    yp, ldy = _mat(out, "out", out_dtype)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [%d, %d]" % (M, N))
     return xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K
@@ -168,6 +180,53 @@ def linear_f16_ex(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None,
     return out
 
 
+def linear_f16_f32out(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor | None = None,
+                      path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """The unrounded FP32 sums x @ weight.T (float16 operands, float32 output)."""
+    xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.float16, torch.float32)
+    rc = _lib().linear_f16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    _check(rc, "linear_f16_f32out")
+    return out
+
+
+def linear_bf16(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """y = BF16(BF16(x @ weight.T) + b) (bfloat16 x [M,K], weight [N,K], b [N])."""
+    if b is None:
+        raise ValueError("linear_bf16 needs a bias; use linear_bf16_nobias")
+    xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out, torch.bfloat16)
+    rc = _lib().linear_bf16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    _check(rc, "linear_bf16")
+    return out
+
+
+def linear_bf16_nobias(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """proj = BF16(x @ weight.T)."""
+    xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.bfloat16)
+    rc = _lib().linear_bf16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    _check(rc, "linear_bf16_nobias")
+    return out
+
+
+def linear_bf16_ex(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None,
+                   out: torch.Tensor | None = None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """linear_bf16 with a forced path and optional bias."""
+    xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out, torch.bfloat16)
+    rc = _lib().linear_bf16_ex(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    _check(rc, "linear_bf16_ex")
+    return out
+
+
+def linear_bf16_f32out(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor | None = None,
+                       path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """The unrounded FP32 sums x @ weight.T (bfloat16 operands, float32 output)."""
+    xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.bfloat16, torch.float32)
+    rc = _lib().linear_bf16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    _check(rc, "linear_bf16_f32out")
+    return out
+
+
 def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,
                     out: torch.Tensor | None = None, path: int = PATH_AUTO) -> dict:
     """The kernel and tile a call would use (host only)."""
@@ -175,9 +234,9 @@ def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | Non
         out = torch.empty((x.shape[0], weight.shape[0]), dtype=torch.float16, device="meta")
         yp, ldy = 0x100000000, max(weight.shape[0], 1)
     else:
-        yp, ldy = _mat(out, "out")
-    xp, ldx = _mat(x, "x")
-    wp, ldw = _mat(weight, "weight")
+        yp, ldy = _mat(out, "out", out.dtype)
+    xp, ldx = _mat(x, "x", x.dtype)
+    wp, ldw = _mat(weight, "weight", weight.dtype)
     p = _Plan()
     rc = _lib().linear_f16_plan(xp, ldx, wp, ldw, None if b is None else b.data_ptr(), yp, ldy,
                                 x.shape[0], weight.shape[0], x.shape[1], int(path), ctypes.byref(p))
@@ -187,7 +246,12 @@ def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | Non
 
 def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None) -> torch.Tensor:
-    """Convenience: the bias call when a bias is given, the projection alone otherwise."""
+    """Convenience: the bias call when a bias is given, the projection alone otherwise;
+    float16 or bfloat16 by x's dtype."""
+    if x.dtype == torch.bfloat16:
+        if bias is None:
+            return linear_bf16_nobias(x, weight, out=out)
+        return linear_bf16(x, weight, bias, out=out)
     if bias is None:
         return linear_f16_nobias(x, weight, out=out)
     return linear_f16(x, weight, bias, out=out)

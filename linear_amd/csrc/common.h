@@ -13,18 +13,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Arguments of one linear-layer launch.  Pointers are device pointers to binary16
-// words; strides in elements.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Arguments of one linear-layer launch.  Pointers are device pointers to 16-bit
+// words (binary16 or bfloat16, per the kernel's element type); y holds 16-bit
+// words or, in the FP32-output mode, floats.  Strides in elements.
 struct LinearArgs {
     const uint16_t* x;   // [M, K], row stride ldx
     const uint16_t* w;   // [N, K], row stride ldw
     const uint16_t* b;   // [N] or nullptr
-    uint16_t* y;         // [M, N], row stride ldy
+    void* y;             // [M, N], row stride ldy
     int64_t ldx, ldw, ldy;
     int M, N, K;
     int tiles_m, tiles_n;
-    int vec_store;       // 1: y 8-byte aligned and ldy % 4 == 0
+    int vec_store;       // 1: y aligned for 4-element vector stores and ldy % 4 == 0
 };
+
+// Element types of x, weight, b and (rounded) y.
+enum : int { kF16 = 0, kBF16 = 1 };
+
+// Output modes: round the FP32 sum to the element type and add the bias (then
+// round again); round only; or store the FP32 sum itself.
+enum : int { kOutBias = 0, kOutRound = 1, kOutF32 = 2 };
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, no stride.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -78,17 +88,77 @@ __device__ inline f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v);
 __device__ inline f16 bits_to_f16(uint16_t u) { return __builtin_bit_cast(f16, u); }
 __device__ inline uint16_t f16_to_bits(f16 h) { return __builtin_bit_cast(uint16_t, h); }
 
-// The epilogue of the contract for one accumulator value: round the FP32 sum to
-// FP16 (round to nearest even), then, with a bias, widen both to FP32, add, and
-// round the sum to FP16.
-template <bool BIAS>
-__device__ inline uint16_t finish(float acc, float bias) {
-    f16 p = (f16)acc;
-    if (BIAS) {
-        f16 yv = (f16)((float)p + bias);
-        return f16_to_bits(yv);
+// Exact widening of a 16-bit word of element type E to FP32.
+template <int E>
+__device__ inline float widen(uint16_t u) {
+    if (E == kF16) return (float)bits_to_f16(u);
+    return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
+// Round an FP32 value to element type E, round to nearest even (v_cvt_f16_f32 /
+// v_cvt_pk_bf16_f32 under the default rounding mode, subnormals kept).
+template <int E>
+__device__ inline uint16_t narrow(float v) {
+    if (E == kF16) return f16_to_bits((f16)v);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// One MFMA step on raw 16-byte operand fragments: FP32 accumulation of exact
+// products (binary16 x binary16 and bfloat16 x bfloat16 products are exact in FP32).
+template <int E>
+__device__ inline f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    if (E == kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int E>
+__device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if (E == kF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The epilogue of the contract for four consecutive output columns nb..nb+3 of
+// row m, and the store.  Rounded modes: round each FP32 sum to E (round to
+// nearest even); with a bias, widen the rounded value and b[n] to FP32, add, and
+// round the sum to E.  FP32 mode: store the sums unrounded.  Columns past N are
+// skipped; rows are checked by the caller.
+template <int E, int MODE>
+__device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, float v1, float v2, float v3) {
+    const float v[4] = {v0, v1, v2, v3};
+    if (MODE == kOutF32) {
+        float* dst = (float*)a.y + (int64_t)m * a.ldy + nb;
+        if (a.vec_store && nb + 3 < a.N) {
+            *(f32x4*)dst = (f32x4){v0, v1, v2, v3};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (nb + e < a.N) dst[e] = v[e];
+        }
+        return;
     }
-    return f16_to_bits(p);
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint16_t p = narrow<E>(v[e]);
+        if (MODE == kOutBias) {
+            const float bias = (nb + e < a.N) ? widen<E>(a.b[nb + e]) : 0.f;
+            p = narrow<E>(widen<E>(p) + bias);
+        }
+        o[e] = p;
+    }
+    uint16_t* dst = (uint16_t*)a.y + (int64_t)m * a.ldy + nb;
+    if (a.vec_store && nb + 3 < a.N) {
+        uint2 u;
+        u.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        u.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *(uint2*)dst = u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) dst[e] = o[e];
+    }
 }
 
 }  // namespace lin

@@ -1,0 +1,7 @@
+// gemm_f16.hip -- the GEMM kernels instantiated for binary16 operands.
+#include "gemm_impl.h"
+
+namespace lin {
+template hipError_t launch_gemm_t<kF16>(int, const LinearArgs&, int, hipStream_t);
+template hipError_t launch_gemm_stream_t<kF16>(int, const LinearArgs&, int, hipStream_t);
+}  // namespace lin

@@ -1,10 +1,13 @@
-// gemm.hip -- MFMA tiled GEMM for the FP16 linear layer on gfx950.
+// gemm_impl.h -- MFMA tiled GEMM for the linear layer on gfx950 (templates).
 //
 // Computes the projection tile C[n, m] = sum_k weight[n, k] * x[m, k] with
-// v_mfma_f32_32x32x16_f16 (exact FP16 products, FP32 accumulation), then the
-// contract's epilogue in registers: round to FP16, and with a bias widen, add
-// b[n] in FP32 and round again ("tensor programs, part 1", section "One Program
-// and One Numerical Contract"; the Inductor capture's cast sequence).
+// v_mfma_f32_32x32x16_f16 / _bf16 (exact products, FP32 accumulation), then the
+// contract's epilogue in registers: round to the element type, and with a bias
+// widen, add b[n] in FP32 and round again ("tensor programs, part 1", section "One
+// Program and One Numerical Contract"; the Inductor capture's cast sequence; for
+// bfloat16, "The Graph IR", op table, ContractionEpilogue: a BF16 head rounds to
+// BF16 before the first epilogue step).  The FP32-output mode stores the sums
+// unrounded (the op table's DenseContraction produces f32).
 //
 // Layout choices:
 //  - The weight tile is the MFMA A operand and the x tile the B operand, so the
@@ -29,6 +32,8 @@
 //    round-robin over the 8 XCDs) owns a contiguous run of tiles, walked in
 //    groups of 8 tile-rows, so tiles running together share x and weight panels
 //    in that XCD's L2.
+#pragma once
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,9 +54,13 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, i
     tn = rem / gm;
 }
 
-template <int BM, int BN, int WM, int WN, bool VEC, bool BIAS>
+// Register-staged variant for layouts the streaming kernel cannot take (K, ldx or
+// ldw not a multiple of 8, or x / weight not 16-byte aligned): every element is
+// loaded with its own masked 2-byte buffer load, staged through registers into the
+// double-buffered LDS tiles.
+template <int BM, int BN, int WM, int WN, int E, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
-gemm_f16_kernel(LinearArgs a) {
+gemm_kernel(LinearArgs a) {
     constexpr int BK = 64;
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;   // one wave's output tile (m x n)
@@ -86,20 +95,11 @@ gemm_f16_kernel(LinearArgs a) {
     u32x4 wreg[CW], xreg[CX];
 
     auto gload = [&](int k0) {
-        if (VEC) {
-            const bool kin = k0 + kc * 8 < K;
-            const uint32_t kb = (uint32_t)k0 * 2u;
+        const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-            for (int i = 0; i < CW; ++i) wreg[i] = load16(rw, kin ? woff[i] + kb : kOOB);
+        for (int i = 0; i < CW; ++i) wreg[i] = load8_masked(rw, woff[i] + kb, k0 + kc * 8, K, true);
 #pragma unroll
-            for (int i = 0; i < CX; ++i) xreg[i] = load16(rx, kin ? xoff[i] + kb : kOOB);
-        } else {
-            const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-            for (int i = 0; i < CW; ++i) wreg[i] = load8_masked(rw, woff[i] + kb, k0 + kc * 8, K, true);
-#pragma unroll
-            for (int i = 0; i < CX; ++i) xreg[i] = load8_masked(rx, xoff[i] + kb, k0 + kc * 8, K, true);
-        }
+        for (int i = 0; i < CX; ++i) xreg[i] = load8_masked(rx, xoff[i] + kb, k0 + kc * 8, K, true);
     };
     auto lds_store = [&](int s) {
         f16* sw = smem + s * STAGE;
@@ -133,16 +133,15 @@ gemm_f16_kernel(LinearArgs a) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int ch = ((ks * 2 + lh) ^ ((lr >> 1) & 7)) << 3;
-            f16x8 av[FN], bv[FM];
+            u32x4 av[FN], bv[FM];
 #pragma unroll
-            for (int i = 0; i < FN; ++i) av[i] = *(const f16x8*)(sw + (wn * TN + i * 32 + lr) * BK + ch);
+            for (int i = 0; i < FN; ++i) av[i] = *(const u32x4*)(sw + (wn * TN + i * 32 + lr) * BK + ch);
 #pragma unroll
-            for (int j = 0; j < FM; ++j) bv[j] = *(const f16x8*)(sx + (wm * TM + j * 32 + lr) * BK + ch);
+            for (int j = 0; j < FM; ++j) bv[j] = *(const u32x4*)(sx + (wm * TM + j * 32 + lr) * BK + ch);
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16<E>(av[i], bv[j], acc[i][j]);
         }
         if (t + 1 < nk) lds_store(cur ^ 1);
         __syncthreads();
@@ -151,37 +150,18 @@ gemm_f16_kernel(LinearArgs a) {
     // Epilogue.  Accumulator element v of block (i, j) sits at
     //   n = n0 + wn*TN + 32 i + 8 (v / 4) + 4 lh + (v % 4),   m = m0 + wm*TM + 32 j + lr.
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int nb = n0 + wn * TN + i * 32 + g * 8 + lh * 4;
-            float bias[4] = {0.f, 0.f, 0.f, 0.f};
-            if (BIAS) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
-            }
 #pragma unroll
             for (int j = 0; j < FM; ++j) {
                 const int m = m0 + wm * TM + j * 32 + lr;
-                if (m >= a.M) continue;
-                uint16_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(acc[i][j][g * 4 + e], bias[e]);
-                uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
-                if (a.vec_store && nb + 3 < a.N) {
-                    uint2 v;
-                    v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                    v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                    *(uint2*)dst = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (nb + e < a.N) dst[e] = o[e];
-                }
+                if (m < a.M)
+                    store4<E, MODE>(a, m, nb, acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                    acc[i][j][g * 4 + 3]);
             }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -208,9 +188,9 @@ gemm_f16_kernel(LinearArgs a) {
 // i.e. row l / CPR, stored chunk l % CPR, so it fetches the logical chunk that the
 // swizzle puts there.  With BK = 64 every load instruction covers whole 128-byte
 // rows.
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, bool BIAS>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
-gemm_f16_stream(LinearArgs a) {
+gemm_stream(LinearArgs a) {
     constexpr int KS = BK / 16;                       // MFMA K steps per slice
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -301,24 +281,24 @@ gemm_f16_stream(LinearArgs a) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 1) * GPW) : "memory");
         __syncthreads();
 
-        f16x8 af[2][FN], bf[2][FM];
+        u32x4 af[2][FN], bf[2][FM];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) af[0][i] = *(const f16x8*)(smem + aoff[0][i]);
+        for (int i = 0; i < FN; ++i) af[0][i] = *(const u32x4*)(smem + aoff[0][i]);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) bf[0][j] = *(const f16x8*)(smem + boff[0][j]);
+        for (int j = 0; j < FM; ++j) bf[0][j] = *(const u32x4*)(smem + boff[0][j]);
 
         auto read_frags = [&](const unsigned char* slot, int ks, int buf) {
 #pragma unroll
-            for (int i = 0; i < FN; ++i) af[buf][i] = *(const f16x8*)(slot + aoff[ks][i]);
+            for (int i = 0; i < FN; ++i) af[buf][i] = *(const u32x4*)(slot + aoff[ks][i]);
 #pragma unroll
-            for (int j = 0; j < FM; ++j) bf[buf][j] = *(const f16x8*)(slot + boff[ks][j]);
+            for (int j = 0; j < FM; ++j) bf[buf][j] = *(const u32x4*)(slot + boff[ks][j]);
         };
         auto mfmas = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma32x32x16<E>(af[buf][i], bf[buf][j], acc[i][j]);
         };
         // K steps 0 .. KS-2 of a slice: read the next step while this one multiplies
         auto inner_steps = [&](const unsigned char* slot) {
@@ -361,113 +341,60 @@ gemm_f16_stream(LinearArgs a) {
 #undef LIN_ISSUE
 
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int nb = n0 + wn * TN + i * 32 + g * 8 + lh * 4;
-            float bias[4] = {0.f, 0.f, 0.f, 0.f};
-            if (BIAS) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
-            }
 #pragma unroll
             for (int j = 0; j < FM; ++j) {
                 const int m = m0 + wm * TM + j * 32 + lr;
-                if (m >= a.M) continue;
-                uint16_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(acc[i][j][g * 4 + e], bias[e]);
-                uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
-                if (a.vec_store && nb + 3 < a.N) {
-                    uint2 v;
-                    v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                    v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                    *(uint2*)dst = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (nb + e < a.N) dst[e] = o[e];
-                }
+                if (m < a.M)
+                    store4<E, MODE>(a, m, nb, acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                    acc[i][j][g * 4 + 3]);
             }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers: one per tile configuration.
+// Launchers (instantiated once per element type in gemm_f16.hip / gemm_bf16.hip).
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_cfg(const LinearArgs& a, bool vec, bool bias, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
-    const dim3 block(WM * WN * 64);
-    LinearArgs args = a;
-    void* params[] = {&args};
-    const void* fn;
-    if (vec) fn = bias ? (const void*)gemm_f16_kernel<BM, BN, WM, WN, true, true>
-                       : (const void*)gemm_f16_kernel<BM, BN, WM, WN, true, false>;
-    else fn = bias ? (const void*)gemm_f16_kernel<BM, BN, WM, WN, false, true>
-                   : (const void*)gemm_f16_kernel<BM, BN, WM, WN, false, false>;
-    return hipLaunchKernel(fn, grid, block, params, 0, stream);
+template <int BM, int BN, int WM, int WN, int E>
+static const void* regstaged_fn(int mode) {
+    if (mode == kOutBias) return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutBias>;
+    if (mode == kOutRound) return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutRound>;
+    return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutF32>;
 }
 
-const GemmConfig kGemmConfigs[kNumGemmConfigs] = {
-    // BM, BN, WM, WN, stages, BK
-    {256, 256, 2, 2, 2, 64},
-    {256, 128, 2, 2, 2, 64},
-    {128, 256, 2, 2, 2, 64},
-    {128, 128, 2, 2, 2, 64},
-    {64, 64, 2, 2, 2, 64},
-};
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E>
+static const void* stream_fn(int mode) {
+    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias>;
+    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound>;
+    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32>;
+}
 
-hipError_t launch_gemm(int cfg, const LinearArgs& a, bool vec, bool bias, hipStream_t stream) {
+static hipError_t launch(const void* fn, const LinearArgs& a, int threads, hipStream_t stream) {
+    LinearArgs args = a;
+    void* params[] = {&args};
+    return hipLaunchKernel(fn, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(threads), params, 0, stream);
+}
+
+template <int E>
+hipError_t launch_gemm_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
     switch (cfg) {
-        case 0: return launch_cfg<256, 256, 2, 2>(a, vec, bias, stream);
-        case 1: return launch_cfg<256, 128, 2, 2>(a, vec, bias, stream);
-        case 2: return launch_cfg<128, 256, 2, 2>(a, vec, bias, stream);
-        case 3: return launch_cfg<128, 128, 2, 2>(a, vec, bias, stream);
-        case 4: return launch_cfg<64, 64, 2, 2>(a, vec, bias, stream);
+        case 0: return launch(regstaged_fn<128, 128, 2, 2, E>(mode), a, 256, stream);
+        case 1: return launch(regstaged_fn<64, 64, 2, 2, E>(mode), a, 256, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BK>
-static hipError_t launch_stream_cfg(const LinearArgs& a, bool bias, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
-    const dim3 block(WM * WN * 64);
-    LinearArgs args = a;
-    void* params[] = {&args};
-    const void* fn = bias ? (const void*)gemm_f16_stream<BM, BN, WM, WN, STAGES, BK, true>
-                          : (const void*)gemm_f16_stream<BM, BN, WM, WN, STAGES, BK, false>;
-    return hipLaunchKernel(fn, grid, block, params, 0, stream);
-}
-
-const GemmConfig kStreamConfigs[kNumStreamConfigs] = {
-    // BM, BN, WM, WN, stages, BK
-    {256, 256, 2, 4, 4, 32},
-    {256, 256, 2, 4, 2, 64},
-    {256, 256, 2, 2, 2, 64},
-    {256, 128, 4, 2, 4, 32},
-    {256, 128, 4, 2, 3, 64},
-    {128, 256, 2, 4, 4, 32},
-    {128, 128, 2, 2, 4, 32},
-    {64, 64, 2, 2, 4, 32},
-    {128, 128, 2, 2, 4, 64},
-    {64, 64, 2, 2, 4, 64},
-};
-
-hipError_t launch_gemm_stream(int cfg, const LinearArgs& a, bool bias, hipStream_t stream) {
+template <int E>
+hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
     switch (cfg) {
-        case 0: return launch_stream_cfg<256, 256, 2, 4, 4, 32>(a, bias, stream);
-        case 1: return launch_stream_cfg<256, 256, 2, 4, 2, 64>(a, bias, stream);
-        case 2: return launch_stream_cfg<256, 256, 2, 2, 2, 64>(a, bias, stream);
-        case 3: return launch_stream_cfg<256, 128, 4, 2, 4, 32>(a, bias, stream);
-        case 4: return launch_stream_cfg<256, 128, 4, 2, 3, 64>(a, bias, stream);
-        case 5: return launch_stream_cfg<128, 256, 2, 4, 4, 32>(a, bias, stream);
-        case 6: return launch_stream_cfg<128, 128, 2, 2, 4, 32>(a, bias, stream);
-        case 7: return launch_stream_cfg<64, 64, 2, 2, 4, 32>(a, bias, stream);
-        case 8: return launch_stream_cfg<128, 128, 2, 2, 4, 64>(a, bias, stream);
-        case 9: return launch_stream_cfg<64, 64, 2, 2, 4, 64>(a, bias, stream);
+        case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E>(mode), a, 512, stream);
+        case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E>(mode), a, 512, stream);
+        case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E>(mode), a, 512, stream);
+        case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E>(mode), a, 256, stream);
+        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E>(mode), a, 256, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,28 +9,44 @@ namespace lin {
 
 struct GemmConfig {
     int bm, bn, wm, wn;   // tile rows (m), tile columns (n), waves along m and n
-    int stages;           // LDS ring depth (streaming kernel); 2 for the register-staged one
+    int stages;           // LDS ring depth
     int bk;               // K elements per slice
 };
 
-// Register-staged MFMA GEMM (any layout).
-constexpr int kNumGemmConfigs = 5;
-extern const GemmConfig kGemmConfigs[kNumGemmConfigs];
-
 // Streaming MFMA GEMM (16-byte aligned layouts), direct-to-LDS K-slice ring.
-constexpr int kNumStreamConfigs = 10;
-extern const GemmConfig kStreamConfigs[kNumStreamConfigs];
+constexpr int kNumStreamConfigs = 5;
+inline constexpr GemmConfig kStreamConfigs[kNumStreamConfigs] = {
+    {256, 256, 2, 4, 2, 64},
+    {256, 128, 4, 2, 3, 64},
+    {128, 256, 2, 4, 4, 32},
+    {128, 128, 2, 2, 4, 64},
+    {64, 64, 2, 2, 4, 64},
+};
 
-// a.tiles_m / a.tiles_n must match the chosen configuration.
-// vec: 16-byte loader (aligned layouts only).
-hipError_t launch_gemm(int cfg, const LinearArgs& a, bool vec, bool bias, hipStream_t stream);
-hipError_t launch_gemm_stream(int cfg, const LinearArgs& a, bool bias, hipStream_t stream);
+// Register-staged MFMA GEMM with element-wise loads (any layout).
+constexpr int kNumGemmConfigs = 2;
+inline constexpr GemmConfig kGemmConfigs[kNumGemmConfigs] = {
+    {128, 128, 2, 2, 2, 64},
+    {64, 64, 2, 2, 2, 64},
+};
+
+// a.tiles_m / a.tiles_n must match the chosen configuration; mode is kOut*.
+template <int E> hipError_t launch_gemm_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream);
+template <int E> hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream);
+
+inline hipError_t launch_gemm(int elem, int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
+    return elem == kBF16 ? launch_gemm_t<kBF16>(cfg, a, mode, stream) : launch_gemm_t<kF16>(cfg, a, mode, stream);
+}
+inline hipError_t launch_gemm_stream(int elem, int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
+    return elem == kBF16 ? launch_gemm_stream_t<kBF16>(cfg, a, mode, stream)
+                         : launch_gemm_stream_t<kF16>(cfg, a, mode, stream);
+}
 
 // Skinny weight-streaming kernel: 16 output columns (n) by 16 rows (m) per
 // workgroup, K split over the workgroup's waves.
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyTile = 16;
 constexpr int kSkinnyKStep = 32;
-hipError_t launch_skinny(const LinearArgs& a, bool vec, bool bias, hipStream_t stream);
+hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream);
 
 }  // namespace lin

@@ -27,9 +27,9 @@ struct Extent {
     uintptr_t lo, hi;  // [lo, hi) in bytes; hi == lo when empty
 };
 
-Extent extent(const void* p, int64_t rows, int64_t ld, int64_t cols) {
+Extent extent(const void* p, int64_t rows, int64_t ld, int64_t cols, int64_t elem_bytes = 2) {
     Extent e{(uintptr_t)p, (uintptr_t)p};
-    if (p && rows > 0 && cols > 0) e.hi = e.lo + (uintptr_t)(((rows - 1) * ld + cols) * 2);
+    if (p && rows > 0 && cols > 0) e.hi = e.lo + (uintptr_t)(((rows - 1) * ld + cols) * elem_bytes);
     return e;
 }
 
@@ -41,11 +41,13 @@ struct Request {
     const uint16_t* w;
     int64_t ldw;
     const uint16_t* b;
-    uint16_t* y;
+    void* y;
     int64_t ldy;
     int64_t M, N, K;
     int32_t path;
     bool need_bias;  // the bias entry point: b must be present
+    int elem;        // lin::kF16 or lin::kBF16
+    bool f32_out;    // y holds the unrounded FP32 sums
 };
 
 // Shape, pointer, stride, alias and path checks.  Pure host logic.
@@ -60,7 +62,7 @@ int32_t validate(const Request& r) {
     if (r.need_bias && !r.b) return LINEAR_E_NULL;
     if (r.ldx < r.K || r.ldw < r.K || r.ldy < r.N) return LINEAR_E_STRIDE;
     if (r.ldx > kMaxLdIn || r.ldw > kMaxLdIn || r.ldy > kMaxLdOut) return LINEAR_E_STRIDE;
-    const Extent ey = extent(r.y, r.M, r.ldy, r.N);
+    const Extent ey = extent(r.y, r.M, r.ldy, r.N, r.f32_out ? 4 : 2);
     if (overlaps(ey, extent(r.x, r.M, r.ldx, r.K))) return LINEAR_E_ALIAS;
     if (overlaps(ey, extent(r.w, r.N, r.ldw, r.K))) return LINEAR_E_ALIAS;
     if (r.b && overlaps(ey, extent(r.b, 1, r.N, r.N))) return LINEAR_E_ALIAS;
@@ -72,29 +74,16 @@ bool vector_loads_ok(const Request& r) {
            (r.ldw % 8 == 0) && (r.K % 8 == 0);
 }
 
-bool vector_store_ok(const Request& r) { return ((uintptr_t)r.y % 8 == 0) && (r.ldy % 4 == 0); }
+bool vector_store_ok(const Request& r) {
+    return ((uintptr_t)r.y % (r.f32_out ? 16 : 8) == 0) && (r.ldy % 4 == 0);
+}
 
-// Tile choice for the register-staged kernel (unaligned layouts): trade tile
-// efficiency (relative rate of one workgroup, larger tiles reuse each loaded
-// byte for more MFMAs) against wave quantization on the 256 CUs.
-const double kCfgRate[lin::kNumGemmConfigs] = {1.00, 0.92, 0.92, 0.80, 0.45};
-
-int choose_gemm_config(int64_t M, int64_t N, int64_t K) {
-    (void)K;
-    int best = 0;
-    double best_t = 1e300;
-    for (int c = 0; c < lin::kNumGemmConfigs; ++c) {
-        const lin::GemmConfig& g = lin::kGemmConfigs[c];
-        const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
-        if (tiles > kMaxGridX / 64) continue;
-        const int64_t waves = (tiles + kNumCUs - 1) / kNumCUs;
-        const double t = (double)waves * (double)g.bm * (double)g.bn / kCfgRate[c];
-        if (t < best_t * 0.999) {
-            best_t = t;
-            best = c;
-        }
-    }
-    return best;
+// Tile choice for the register-staged kernel (unaligned layouts, not tuned): the
+// larger tile when it still gives every CU a tile.
+int choose_gemm_config(int64_t M, int64_t N) {
+    const lin::GemmConfig& g = lin::kGemmConfigs[0];
+    const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+    return tiles >= kNumCUs ? 0 : 1;
 }
 
 // Tile choice for the streaming kernel (aligned layouts).  Measured on MI355X, a
@@ -105,11 +94,11 @@ struct StreamChoice {
     int cfg;
     double rate;   // sustained throughput relative to the 256x256 tile
 };
-// configurations 1, 4, 5, 8, 9 of kStreamConfigs: 256x256, 256x128, 128x256, 128x128, 64x64
-const StreamChoice kStreamOrder[] = {{1, 1.00}, {4, 0.94}, {5, 0.85}, {8, 0.80}, {9, 0.57}};
+// kStreamConfigs in order: 256x256, 256x128, 128x256, 128x128, 64x64
+const StreamChoice kStreamOrder[] = {{0, 1.00}, {1, 0.94}, {2, 0.85}, {3, 0.80}, {4, 0.57}};
 
 int choose_stream_config(int64_t M, int64_t N) {
-    int best = 9;
+    int best = 4;
     double best_score = -1.0;
     for (const StreamChoice& c : kStreamOrder) {
         const lin::GemmConfig& g = lin::kStreamConfigs[c.cfg];
@@ -141,7 +130,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         p->grid = gx * gy;
     } else {
         const bool stream = p->vector_io != 0;
-        const int c = stream ? choose_stream_config(r.M, r.N) : choose_gemm_config(r.M, r.N, r.K);
+        const int c = stream ? choose_stream_config(r.M, r.N) : choose_gemm_config(r.M, r.N);
         const lin::GemmConfig& g = stream ? lin::kStreamConfigs[c] : lin::kGemmConfigs[c];
         p->tile_m = g.bm;
         p->tile_n = g.bn;
@@ -199,25 +188,25 @@ int32_t run(const Request& r, void* stream) {
     a.N = (int)r.N;
     a.K = (int)r.K;
     a.vec_store = vector_store_ok(r) ? 1 : 0;
-    const bool bias = r.b != nullptr;
+    const int mode = r.f32_out ? lin::kOutF32 : (r.b != nullptr ? lin::kOutBias : lin::kOutRound);
     const bool vec = p.vector_io != 0;
     hipError_t e;
     if (p.path == LINEAR_PATH_SKINNY) {
         a.tiles_m = (int)((r.M + 15) / 16);
         a.tiles_n = (int)((r.N + 15) / 16);
-        e = lin::launch_skinny(a, vec, bias, (hipStream_t)stream);
+        e = lin::launch_skinny(r.elem, a, vec, mode, (hipStream_t)stream);
     } else if (vec) {
         const int c = choose_stream_config(r.M, r.N);
         const lin::GemmConfig& g = lin::kStreamConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
-        e = lin::launch_gemm_stream(c, a, bias, (hipStream_t)stream);
+        e = lin::launch_gemm_stream(r.elem, c, a, mode, (hipStream_t)stream);
     } else {
-        const int c = choose_gemm_config(r.M, r.N, r.K);
+        const int c = choose_gemm_config(r.M, r.N);
         const lin::GemmConfig& g = lin::kGemmConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
-        e = lin::launch_gemm(c, a, vec, bias, (hipStream_t)stream);
+        e = lin::launch_gemm(r.elem, c, a, mode, (hipStream_t)stream);
     }
     if (e != hipSuccess) {
         g_last_hip_error = (int32_t)e;
@@ -233,20 +222,54 @@ extern "C" {
 int32_t linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
                    const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                    void* stream) {
-    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, LINEAR_PATH_AUTO, true};
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, LINEAR_PATH_AUTO, true, lin::kF16, false};
     return run(r, stream);
 }
 
 int32_t linear_f16_nobias(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
-    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, LINEAR_PATH_AUTO, false};
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, LINEAR_PATH_AUTO, false, lin::kF16, false};
     return run(r, stream);
 }
 
 int32_t linear_f16_ex(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
                       const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                       int32_t path, void* stream) {
-    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false};
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false, lin::kF16, false};
+    return run(r, stream);
+}
+
+int32_t linear_f16_f32out(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                          float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t path,
+                          void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kF16, true};
+    return run(r, stream);
+}
+
+int32_t linear_bf16(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                    const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                    void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, LINEAR_PATH_AUTO, true, lin::kBF16, false};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_nobias(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, LINEAR_PATH_AUTO, false, lin::kBF16, false};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_ex(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                       const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                       int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false, lin::kBF16, false};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_f32out(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                           float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t path,
+                           void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kBF16, true};
     return run(r, stream);
 }
 
@@ -254,7 +277,7 @@ int32_t linear_f16_plan(const uint16_t* x, int64_t ldx, const uint16_t* weight, 
                         const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         int32_t path, linear_plan* out) {
     if (!out) return LINEAR_E_NULL;
-    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false};
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false, lin::kF16, false};
     int32_t st = validate(r);
     if (st != LINEAR_OK) return st;
     if (M == 0 || N == 0) {

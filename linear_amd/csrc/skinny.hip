@@ -1,4 +1,5 @@
-// skinny.hip -- the small-M (decode) path of the FP16 linear layer on gfx950.
+// skinny.hip -- the small-M (decode) path of the linear layer on gfx950
+// (binary16 or bfloat16 operands; rounded, biased or FP32 output, as the GEMM).
 //
 // For M <= 16 the layer is a weight stream: every weight element is used by at
 // most 16 rows of x, so the time is the time to read weight[N, K] once from HBM.
@@ -17,22 +18,22 @@
 // lanes of one row read 64 contiguous bytes, and A and B always pair the same K.
 //
 // Two variants:
-//  - skinny_f16_stream (16-byte aligned layouts): per pass of up to 16 MFMA steps
+//  - skinny_stream (16-byte aligned layouts): per pass of up to 16 MFMA steps
 //    a wave first copies the rows of x it needs straight into its own LDS region
 //    (one contiguous 1 KB direct-to-LDS load per x row, so at M = 1 a single
 //    instruction instead of one per step), then issues all of its weight loads
 //    back to back (a scheduling barrier keeps the compiler from interleaving them
 //    with the MFMAs, so every load is in flight at once), and consumes each weight
 //    fragment as it arrives.
-//  - skinny_f16_kernel (any layout): element-wise masked loads of both operands.
+//  - skinny_kernel (any layout): element-wise masked loads of both operands.
 #include "common.h"
 #include "kernels.h"
 
 namespace lin {
 
-template <int WAVES, bool BIAS>
+template <int WAVES, int E, int MODE>
 __global__ void __launch_bounds__(WAVES * 64)
-skinny_f16_stream(LinearArgs a) {
+skinny_stream(LinearArgs a) {
     constexpr int PU = 16;                    // MFMA steps (32 K values each) per pass
     constexpr int XPITCH = PU * 64 + 16;      // bytes per LDS row of x: 512 halves + pad
     __shared__ __attribute__((aligned(16))) unsigned char xs[WAVES * 16 * XPITCH];
@@ -78,7 +79,7 @@ skinny_f16_stream(LinearArgs a) {
             const uint32_t keep = (row < mv && k < kend) ? 0xffffffffu : 0u;
             u32x4 xv = *(const u32x4*)(xreg + row * XPITCH + (s * 4 + grp) * 16);
             xv &= (u32x4){keep, keep, keep, keep};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wa[s]), as_f16x8(xv), acc, 0, 0, 0);
+            acc = mfma16x16x32<E>(wa[s], xv, acc);
         }
         // every LDS read of this pass has been consumed by an MFMA above, so the
         // next pass may overwrite the region
@@ -91,34 +92,15 @@ skinny_f16_stream(LinearArgs a) {
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) s += red[w][lane];
 
+    // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
     const int m = m0 + (lane & 15);
     const int nb = n0 + (lane >> 4) * 4;
-    if (m >= a.M) return;
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (BIAS) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
-    }
-    uint16_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(s[e], bias[e]);
-    uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
-    if (a.vec_store && nb + 3 < a.N) {
-        uint2 v;
-        v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-        v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-        *(uint2*)dst = v;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (nb + e < a.N) dst[e] = o[e];
-    }
+    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3]);
 }
 
-template <int WAVES, bool VEC, bool BIAS>
+template <int WAVES, int E, int MODE>
 __global__ void __launch_bounds__(WAVES * 64)
-skinny_f16_kernel(LinearArgs a) {
+skinny_kernel(LinearArgs a) {
     constexpr int UNROLL = 8;
     const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -142,18 +124,12 @@ skinny_f16_kernel(LinearArgs a) {
         for (int s = 0; s < UNROLL; ++s) {
             const int k = ((u + s) * 4 + grp) * 8;   // first K of this lane's chunk
             const bool in = (u + s) < ue;
-            if (VEC) {
-                const bool kin = in && k < K;
-                wa[s] = load16(rw, (kin && w_ok) ? wrow + 2u * (uint32_t)k : kOOB);
-                xb[s] = load16(rx, (kin && x_ok) ? xrow + 2u * (uint32_t)k : kOOB);
-            } else {
-                wa[s] = load8_masked(rw, wrow + 2u * (uint32_t)k, k, in ? K : 0, w_ok);
-                xb[s] = load8_masked(rx, xrow + 2u * (uint32_t)k, k, in ? K : 0, x_ok);
-            }
+            wa[s] = load8_masked(rw, wrow + 2u * (uint32_t)k, k, in ? K : 0, w_ok);
+            xb[s] = load8_masked(rx, xrow + 2u * (uint32_t)k, k, in ? K : 0, x_ok);
         }
 #pragma unroll
         for (int s = 0; s < UNROLL; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wa[s]), as_f16x8(xb[s]), acc, 0, 0, 0);
+            acc = mfma16x16x32<E>(wa[s], xb[s], acc);
     }
 
     __shared__ f32x4 red[WAVES][64];
@@ -167,39 +143,27 @@ skinny_f16_kernel(LinearArgs a) {
     // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
     const int m = m0 + (lane & 15);
     const int nb = n0 + (lane >> 4) * 4;
-    if (m >= a.M) return;
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (BIAS) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (nb + e < a.N) bias[e] = (float)bits_to_f16(a.b[nb + e]);
-    }
-    uint16_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = finish<BIAS>(s[e], bias[e]);
-    uint16_t* dst = a.y + (int64_t)m * a.ldy + nb;
-    if (a.vec_store && nb + 3 < a.N) {
-        uint2 v;
-        v.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-        v.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-        *(uint2*)dst = v;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (nb + e < a.N) dst[e] = o[e];
-    }
+    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3]);
 }
 
-hipError_t launch_skinny(const LinearArgs& a, bool vec, bool bias, hipStream_t stream) {
+template <int E>
+static const void* skinny_fn(bool vec, int mode) {
+    if (vec) {
+        if (mode == kOutBias) return (const void*)skinny_stream<kSkinnyWaves, E, kOutBias>;
+        if (mode == kOutRound) return (const void*)skinny_stream<kSkinnyWaves, E, kOutRound>;
+        return (const void*)skinny_stream<kSkinnyWaves, E, kOutF32>;
+    }
+    if (mode == kOutBias) return (const void*)skinny_kernel<kSkinnyWaves, E, kOutBias>;
+    if (mode == kOutRound) return (const void*)skinny_kernel<kSkinnyWaves, E, kOutRound>;
+    return (const void*)skinny_kernel<kSkinnyWaves, E, kOutF32>;
+}
+
+hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream) {
     const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
     const dim3 block(kSkinnyWaves * 64);
     LinearArgs args = a;
     void* params[] = {&args};
-    const void* fn;
-    if (vec) fn = bias ? (const void*)skinny_f16_stream<kSkinnyWaves, true>
-                       : (const void*)skinny_f16_stream<kSkinnyWaves, false>;
-    else fn = bias ? (const void*)skinny_f16_kernel<kSkinnyWaves, false, true>
-                   : (const void*)skinny_f16_kernel<kSkinnyWaves, false, false>;
+    const void* fn = elem == kBF16 ? skinny_fn<kBF16>(vec, mode) : skinny_fn<kF16>(vec, mode);
     return hipLaunchKernel(fn, grid, block, params, 0, stream);
 }
 

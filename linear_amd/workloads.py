@@ -61,48 +61,52 @@ WORKLOADS = {
 DECODE_STEP = ("gemv1", "gemv16")
 
 
-def make_inputs(M: int, N: int, K: int, a: float, seed: int = 0, device: str = "cpu"):
-    """Draw (x, weight, b) as contiguous float16 tensors, following the recipe above."""
+def make_inputs(M: int, N: int, K: int, a: float, seed: int = 0, device: str = "cpu",
+                dtype: torch.dtype = torch.float16):
+    """Draw (x, weight, b) as contiguous float16 (or bfloat16) tensors, following the
+    recipe above; the float32 draws are the same for both element types."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     x = torch.randn((M, K), generator=g, dtype=torch.float32)
     w = torch.rand((N, K), generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0).mul_(a)
     b = torch.rand((N,), generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0).mul_(a)
-    x16, w16, b16 = x.to(torch.float16), w.to(torch.float16), b.to(torch.float16)
+    x16, w16, b16 = x.to(dtype), w.to(dtype), b.to(dtype)
     if device != "cpu":
         x16, w16, b16 = x16.to(device), w16.to(device), b16.to(device)
     return x16, w16, b16
 
 
-def workload_inputs(name: str, seed: int = 0, device: str = "cpu"):
+def workload_inputs(name: str, seed: int = 0, device: str = "cpu", dtype: torch.dtype = torch.float16):
     wl = WORKLOADS[name]
-    return make_inputs(wl.M, wl.N, wl.K, wl.a, seed=seed, device=device)
+    return make_inputs(wl.M, wl.N, wl.K, wl.a, seed=seed, device=device, dtype=dtype)
 
 
 def small_integers(M: int, N: int, K: int, seed: int = 0, lo: int = -3, hi: int = 3,
-                   blo: int = -8, bhi: int = 8):
-    """Integer-valued float16 tensors: x, weight in [lo, hi], b in [blo, bhi].
+                   blo: int = -8, bhi: int = 8, dtype: torch.dtype = torch.float16):
+    """Integer-valued float16 (or bfloat16) tensors: x, weight in [lo, hi], b in [blo, bhi].
 
     With sum |x*w| < 2^24 every partial sum in every order is an exact FP32
     integer, so the result is unique whatever the summation order."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
-    x = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float16)
-    w = torch.randint(lo, hi + 1, (N, K), generator=g).to(torch.float16)
-    b = torch.randint(blo, bhi + 1, (N,), generator=g).to(torch.float16)
+    x = torch.randint(lo, hi + 1, (M, K), generator=g).to(dtype)
+    w = torch.randint(lo, hi + 1, (N, K), generator=g).to(dtype)
+    b = torch.randint(blo, bhi + 1, (N,), generator=g).to(dtype)
     return x, w, b
 
 
-def random_words(shape, seed: int = 0, finite: bool = True):
-    """Uniformly random binary16 bit patterns (optionally finite only) as float16."""
+def random_words(shape, seed: int = 0, finite: bool = True, dtype: torch.dtype = torch.float16):
+    """Uniformly random 16-bit patterns (optionally finite only) as float16 or bfloat16."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     words = torch.randint(0, 1 << 16, shape, generator=g, dtype=torch.int32)
     if finite:
-        # exponent field 31 is inf/NaN: clear its top bit so the field becomes 15
-        e31 = (words & 0x7C00) == 0x7C00
-        words = torch.where(e31, words & ~0x4000, words)
-    return words.to(torch.int16).view(torch.float16)
+        # the all-ones exponent field is inf/NaN: clear its top bit
+        # (binary16: field 31 -> 15; bfloat16: field 255 -> 127)
+        emask, top = (0x7F80, 0x4000) if dtype == torch.bfloat16 else (0x7C00, 0x4000)
+        eall = (words & emask) == emask
+        words = torch.where(eall, words & ~top, words)
+    return words.to(torch.int16).view(dtype)
 
 
 def sample_points(M: int, N: int, count: int, seed: int = 0):

@@ -127,15 +127,20 @@ def test_one_hot_weights(orc, path):
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
-def test_k1_and_k2_unique_results(orc, path):
-    for K in (1, 2):
-        x = workloads.random_words((64, K), seed=40 + K)
-        w = workloads.random_words((96, K), seed=50 + K)
-        b = workloads.random_words((96,), seed=60 + K)
-        if K == 2:  # keep the two products finite so the sum is well defined
-            x = (torch.randn(64, 2, generator=torch.Generator().manual_seed(7)) * 8).to(torch.float16)
-            w = (torch.randn(96, 2, generator=torch.Generator().manual_seed(8)) * 8).to(torch.float16)
-        full_check(orc, x, w, b, path, exact=True)
+def test_k1_unique_and_k2_within_rule(orc, path):
+    """K = 1 is one exact product rounded once: unique, bit-exact.  K = 2 is one
+    FP32 addition, but the matrix-core step may cut the smaller product below the
+    guard bit, so it is held to the acceptance rule (the K = 2 results that are
+    unique on the GPU too, ties on the guard grid, are checked bit for bit with
+    the FP32-output tests)."""
+    x = workloads.random_words((64, 1), seed=41)
+    w = workloads.random_words((96, 1), seed=51)
+    b = workloads.random_words((96,), seed=61)
+    full_check(orc, x, w, b, path, exact=True)
+    x = (torch.randn(64, 2, generator=torch.Generator().manual_seed(7)) * 8).to(torch.float16)
+    w = (torch.randn(96, 2, generator=torch.Generator().manual_seed(8)) * 8).to(torch.float16)
+    b = workloads.random_words((96,), seed=62)
+    full_check(orc, x, w, b, path)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)

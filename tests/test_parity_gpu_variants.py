@@ -1,0 +1,423 @@
+"""Parity of the bfloat16 and FP32-output entry points against the CPU oracle (gfx950 GPU).
+
+bfloat16: the same layer with bfloat16 operands, projection and output ("The
+Graph IR", op table: Cast to bf16 and the BF16 contraction head).  FP32 output:
+the unrounded sums (the op table's DenseContraction with an f32 result).
+Acceptance as for binary16: the rule of oracle/tolerance.py with the element
+type's ulp, the rigorous outer band, and bit-for-bit equality where the result
+is unique (integer data, K <= 2, identity and one-hot weights).  The FP32
+sums are held to the forward-error bound of FP32 summation in any order, and
+must round to exactly the bias-less call's projection (same kernel, same order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_amd as la
+from linear_amd import workloads
+from oracle import tolerance
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF = torch.bfloat16
+F16 = torch.float16
+PATHS = [la.PATH_GEMM, la.PATH_SKINNY]
+PATH_IDS = ["gemm", "skinny"]
+
+
+def words(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().numpy()
+
+
+def eq_words(a, b, elem):
+    a = np.asarray(a, np.uint16)
+    b = np.asarray(b, np.uint16)
+    fa, fb = tolerance.words_to_f64(a, elem), tolerance.words_to_f64(b, elem)
+    return (a == b) | (np.isnan(fa) & np.isnan(fb)) | ((fa == 0) & (fb == 0))
+
+
+def eq_f32(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b)) | ((a == 0) & (b == 0))
+
+
+def elem_of(dtype):
+    return tolerance.BF16 if dtype == BF else tolerance.F16
+
+
+def call(x, w, b, path, dtype):
+    xd, wd = x.to(DEV), w.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    fn = la.linear_bf16_ex if dtype == BF else la.linear_f16_ex
+    y = fn(xd, wd, bd, path=path)
+    torch.cuda.synchronize()
+    return y
+
+
+def call_sums(x, w, path, dtype, out=None):
+    fn = la.linear_bf16_f32out if dtype == BF else la.linear_f16_f32out
+    s = fn(x.to(DEV), w.to(DEV), out=out, path=path)
+    torch.cuda.synchronize()
+    return s
+
+
+def full_check(orc, x, w, b, path, dtype, exact=False):
+    """Bias-less call, bias call and FP32-output call on the GPU against the oracle."""
+    elem = elem_of(dtype)
+    K = x.shape[1]
+    p_gpu = words(call(x, w, None, path, dtype))
+    y_gpu = words(call(x, w, b, path, dtype))
+    s_gpu = f32(call_sums(x, w, path, dtype))
+    y_ref, p_ref, s_ref = orc.linear(x, w, b, elem=elem, sums=True)
+    bb = np.broadcast_to(words(b)[None, :], y_ref.shape).copy()
+    assert eq_words(y_gpu, orc.bias_epilogue(p_gpu, bb, elem=elem), elem).all(), "y is not the epilogue of proj"
+    narrow = orc.f32_to_bf16 if dtype == BF else orc.f32_to_f16
+    assert eq_words(narrow(s_gpu), p_gpu, elem).all(), "FP32 sums do not round to the projection"
+    if exact:
+        assert eq_f32(s_gpu, s_ref).all(), "FP32 sums differ (exact case): %d" % (~eq_f32(s_gpu, s_ref)).sum()
+        assert eq_words(p_gpu, p_ref, elem).all(), "proj differs (exact case): %d" % (~eq_words(p_gpu, p_ref, elem)).sum()
+        assert eq_words(y_gpu, y_ref, elem).all(), "y differs (exact case)"
+        return
+    S, A = orc.band(x, w, elem=elem)
+    ok, rep = tolerance.check_sums(s_gpu, S, A, K)
+    assert ok.all(), rep
+    ok, rep = tolerance.check_proj(p_gpu, p_ref, A, elem=elem)
+    assert ok.all(), rep
+    ok, rep = tolerance.check_y(y_gpu, y_ref, p_ref, A, elem=elem)
+    assert ok.all(), rep
+    assert tolerance.in_outer_band(p_gpu, S, A, K, elem=elem).all(), "outside the outer band"
+
+
+def normal_words(shape, seed, dtype=BF, lo=-30, hi=30):
+    """Finite normal values with exponents in [lo, hi] and random sign and fraction bits."""
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand(shape, generator=g) + 1.0
+    e = torch.randint(lo, hi + 1, shape, generator=g).to(torch.float32)
+    s = torch.randint(0, 2, shape, generator=g).to(torch.float32) * 2 - 1
+    return (s * m * torch.pow(2.0, e)).to(dtype)
+
+
+# --------------------------------------------------------------------- bfloat16, exact cases
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 9, 1), (17, 23, 300), (300, 257, 1000),
+                                   (16, 4096, 512), (70, 130, 8), (3, 5, 7), (129, 66, 131)])
+def test_bf16_small_integers_bit_exact(orc, path, M, N, K):
+    x, w, b = workloads.small_integers(M, N, K, seed=M + N + K, dtype=BF)
+    full_check(orc, x, w, b, path, BF, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_integer_ties_bit_exact(orc, path):
+    """Integer sums where bfloat16's 8-bit significand forces ties and round-ups:
+    odd integers in (256, 512), 2 mod 4 in (512, 1024), and so on; then the bias."""
+    rows = []
+    for s in (257, 259, 261, 383, 514, 518, 770, 1029, 1031, 4097, 16387, -257, -514, -1031):
+        v = [0.0] * 160
+        rest = float(s)
+        for k in range(160):
+            step = max(min(rest, 128.0), -128.0)
+            v[k] = step
+            rest -= step
+        assert rest == 0
+        rows.append(v)
+    x = torch.tensor(rows, dtype=BF)
+    w = torch.ones(40, 160, dtype=BF)
+    b = torch.tensor([(-1.0) ** i * (i % 7) for i in range(40)], dtype=BF)
+    full_check(orc, x, w, b, path, BF, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_identity_weights(orc, path):
+    x = normal_words((40, 96), seed=30)
+    w = torch.eye(96, dtype=BF)
+    b = normal_words((96,), seed=31)
+    full_check(orc, x, w, b, path, BF, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_one_hot_weights(orc, path):
+    g = np.random.default_rng(32)
+    M, N, K = 33, 70, 50
+    x = normal_words((M, K), seed=33)
+    pi = g.integers(0, K, N)
+    e = g.integers(-4, 5, N)
+    w = torch.zeros(N, K, dtype=torch.float32)
+    w[torch.arange(N), torch.from_numpy(pi)] = torch.from_numpy((2.0 ** e).astype(np.float32))
+    full_check(orc, x, w.to(BF), torch.zeros(N, dtype=BF), path, BF, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_k1_unique_result(orc, path):
+    """K = 1: one exact product rounded once, a unique result."""
+    x = normal_words((64, 1), seed=41)
+    w = normal_words((96, 1), seed=51)
+    b = normal_words((96,), seed=61)
+    full_check(orc, x, w, b, path, BF, exact=True)
+
+
+def k2_guard_grid_ties(dtype, seed):
+    """K = 2 sums a*2^s + c*2^(s-g) whose FP32 rounding is a tie or near-tie: the
+    second product sits on the grid one bit below the first's FP32 last place, so
+    every FP32 accumulation (IEEE or a matrix-core step) must give RNE of the exact
+    sum.  binary16: a in [1024, 2048), c odd or even integer, g = 14; bfloat16:
+    a in [128, 256), g = 17."""
+    lo, g = (1024, 14) if dtype == F16 else (128, 17)
+    gen = torch.Generator().manual_seed(seed)
+    M, N = 64, 56
+    a = torch.randint(lo, 2 * lo, (M,), generator=gen).to(torch.float64)
+    c = torch.randint(-(lo - 1), lo, (M,), generator=gen).to(torch.float64)
+    x = torch.stack([a, c], 1).to(dtype)
+    sh = torch.randint(-3, 4, (N,), generator=gen).to(torch.float64)
+    w = torch.stack([torch.pow(2.0, sh), torch.pow(2.0, sh - g)], 1).to(dtype)
+    b = torch.randint(-8, 9, (N,), generator=gen).to(dtype)
+    return x, w, b
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_k2_fp32_ties_on_the_guard_grid_bit_exact(orc, path, dtype):
+    x, w, b = k2_guard_grid_ties(dtype, seed=44)
+    # half of the sums are exact FP32 ties (c odd): RNE must pick the even neighbour
+    full_check(orc, x, w, b, path, dtype, exact=True)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_k2_wide_exponent_spread_within_bound(orc, path, dtype):
+    """K = 2 with products 2^-60..2^60 apart (bfloat16) or 2^-28..2^28 (binary16):
+    the matrix-core step drops bits below the guard bit, so the FP32 sum is within
+    one FP32 ulp of the exact sum (not always its RNE) and the rounded outputs obey
+    the acceptance rule."""
+    lo, hi = (-30, 30) if dtype == BF else (-14, 14)
+    x = normal_words((64, 2), seed=42, dtype=dtype, lo=lo, hi=hi)
+    w = normal_words((96, 2), seed=52, dtype=dtype, lo=lo, hi=hi)
+    b = normal_words((96,), seed=62, dtype=dtype, lo=lo, hi=hi)
+    full_check(orc, x, w, b, path, dtype)
+    s = f32(call_sums(x, w, path, dtype)).astype(np.float64)
+    S, _ = orc.band(x, w, elem=elem_of(dtype))
+    ulp32 = np.spacing(np.abs(S).astype(np.float32)).astype(np.float64)
+    assert (np.abs(s - S) < ulp32).all(), "a two-term FP32 sum is off by a full FP32 ulp"
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_accumulation_step_drops_bits_below_the_guard_bit(orc, path, dtype):
+    """The matrix-core accumulation behaviour the acceptance bound is built on:
+    1 + 1.75*2^-24 gives 1 (IEEE FP32 would give 1 + 2^-23; the term is cut to
+    2^-24 and the tie goes to even), 1 - 0.75*2^-24 gives 1, and terms on the
+    guard grid round to nearest even as in IEEE.  Each result is within one FP32
+    ulp of the exact sum."""
+    if dtype == F16:   # products through w = 2^-14
+        xs = [[1.0, 1.75 * 2.0 ** -10], [1.0, -0.75 * 2.0 ** -10], [1.0, 2.0 ** -10], [1.0, 3 * 2.0 ** -10]]
+        w = torch.tensor([[1.0, 2.0 ** -14]], dtype=torch.float64).to(dtype)
+    else:
+        xs = [[1.0, 1.75 * 2.0 ** -24], [1.0, -0.75 * 2.0 ** -24], [1.0, 2.0 ** -24], [1.0, 3 * 2.0 ** -24]]
+        w = torch.tensor([[1.0, 1.0]], dtype=torch.float64).to(dtype)
+    x = torch.tensor(xs, dtype=torch.float64).to(dtype)
+    s = f32(call_sums(x, w, path, dtype))[:, 0]
+    exp = np.array([1.0, 1.0, 1.0, 1.0 + 2.0 ** -22], np.float32)
+    assert np.array_equal(s.view(np.uint32), exp.view(np.uint32)), s
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_subnormal_operands_bit_exact(orc, path):
+    """bfloat16 subnormals (FP32 subnormals, multiples of 2^-133) against small
+    integers: every partial sum is an exact multiple of 2^-133, so the result is
+    unique; a flush to zero of inputs, products or sums would show."""
+    g = torch.Generator().manual_seed(21)
+    xs = (torch.randint(-127, 128, (48, 256), generator=g).to(torch.float64) * 2.0 ** -133).to(BF)
+    assert (xs.view(torch.int16) & 0x7F80 == 0).all()
+    wi = torch.randint(-3, 4, (80, 256), generator=g).to(BF)
+    b = (torch.randint(-50, 51, (80,), generator=g).to(torch.float64) * 2.0 ** -133).to(BF)
+    full_check(orc, xs, wi, b, path, BF, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_k0_is_the_empty_sum(orc, path):
+    b = normal_words((37,), seed=70)
+    x = torch.zeros(5, 0, dtype=BF)
+    w = torch.zeros(37, 0, dtype=BF)
+    y = words(call(x, w, b, path, BF))
+    assert eq_words(y, np.broadcast_to(words(b), (5, 37)), tolerance.BF16).all()
+    assert (words(call(x, w, None, path, BF)) == 0).all()
+    s = f32(call_sums(x, w, path, BF))
+    assert (s.view(np.uint32) == 0).all(), "the empty sum is +0"
+
+
+def test_bf16_nan_and_inf_propagate(orc):
+    x, w, b = workloads.make_inputs(40, 48, 64, 0.1, seed=71, dtype=BF)
+    x[3, 5] = float("nan")
+    w[7, 9] = float("inf")
+    for path in PATHS:
+        y = words(call(x, w, b, path, BF))
+        y_ref, _ = orc.linear(x, w, b, elem=tolerance.BF16)
+        eq = eq_words(y, y_ref, tolerance.BF16)
+        assert eq[:, 7].all() and eq[3].all()
+        assert np.isnan(tolerance.words_to_f64(y[3], tolerance.BF16)).all()
+
+
+# --------------------------------------------------------------------- bfloat16, random data
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (1, 4096, 4096), (16, 4096, 4096), (7, 1000, 520),
+                                   (33, 65, 100), (257, 129, 72), (200, 300, 520), (512, 384, 1024),
+                                   (3, 5, 7), (130, 70, 333)])
+def test_bf16_random_ragged_shapes(orc, path, M, N, K):
+    x, w, b = workloads.make_inputs(M, N, K, 1.0 / np.sqrt(max(K, 1)), seed=M * 7 + N * 3 + K, dtype=BF)
+    full_check(orc, x, w, b, path, BF)
+
+
+@pytest.mark.parametrize("name", ["toy", "gemv1", "gemv16"])
+def test_bf16_workloads_full(orc, name):
+    x, w, b = workloads.workload_inputs(name, seed=0, dtype=BF)
+    full_check(orc, x, w, b, la.PATH_AUTO, BF)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("name", ["attn", "down"])
+def test_full_size_sampled_with_sums(orc, name, dtype):
+    """Full-size prefill shapes in the benchmark's launch configuration: sampled
+    outputs of all three calls against the oracle, properties over every output."""
+    elem = elem_of(dtype)
+    x, w, b = workloads.workload_inputs(name, seed=0, dtype=dtype)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    if dtype == BF:
+        p, y, s = la.linear_bf16_nobias(xd, wd), la.linear_bf16(xd, wd, bd), la.linear_bf16_f32out(xd, wd)
+        s2 = la.linear_bf16_f32out(xd, wd)
+    else:
+        p, y, s = la.linear_f16_nobias(xd, wd), la.linear_f16(xd, wd, bd), la.linear_f16_f32out(xd, wd)
+        s2 = la.linear_f16_f32out(xd, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(s.view(torch.int32), s2.view(torch.int32)), "rerun not bit-identical"
+    pw, yw = words(p), words(y)
+    assert np.isfinite(tolerance.words_to_f64(yw, elem)).all()
+    # the FP32 sums round to the projection, and y is its epilogue, everywhere
+    narrow = torch.bfloat16 if dtype == BF else torch.float16
+    assert torch.equal(s.to(narrow).view(torch.int16), p.view(torch.int16)), \
+        "FP32 sums do not round to the projection"
+    bb = np.broadcast_to(words(b)[None, :], yw.shape).copy()
+    assert eq_words(yw, orc.bias_epilogue(pw, bb, elem=elem), elem).all()
+    del p, y, s2
+    ms, ns = workloads.sample_points(x.shape[0], w.shape[0], 8192, seed=2)
+    r = orc.points(x, w, b, ms, ns, elem=elem)
+    sw = f32(s)[ms, ns]
+    K = x.shape[1]
+    ok, rep = tolerance.check_sums(sw, r["S"], r["A"], K)
+    assert ok.all(), rep
+    ok, rep = tolerance.check_proj(pw[ms, ns], r["proj"], r["A"], elem=elem)
+    assert ok.all(), rep
+    ok, rep = tolerance.check_y(yw[ms, ns], r["y"], r["proj"], r["A"], elem=elem)
+    assert ok.all(), rep
+    assert tolerance.in_outer_band(pw[ms, ns], r["S"], r["A"], K, elem=elem).all()
+
+
+# --------------------------------------------------------------------- FP32 output (binary16 operands)
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (17, 23, 300), (300, 257, 1000), (16, 4096, 512), (3, 5, 7)])
+def test_f16_sums_small_integers_bit_exact(orc, path, M, N, K):
+    x, w, b = workloads.small_integers(M, N, K, seed=M + N + K + 1)
+    full_check(orc, x, w, b, path, F16, exact=True)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (7, 1000, 520), (257, 129, 72), (512, 384, 1024),
+                                   (130, 70, 333)])
+def test_f16_sums_random_ragged_shapes(orc, path, M, N, K):
+    x, w, b = workloads.make_inputs(M, N, K, 1.0 / np.sqrt(K), seed=M * 5 + N + K)
+    full_check(orc, x, w, b, path, F16)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_sums_k0_and_specials(orc, path):
+    x = torch.zeros(5, 0, dtype=F16)
+    w = torch.zeros(37, 0, dtype=F16)
+    assert (f32(call_sums(x, w, path, F16)).view(np.uint32) == 0).all()
+    x, w, _ = workloads.make_inputs(40, 48, 64, 0.1, seed=72)
+    x[3, 5] = float("nan")
+    w[7, 9] = float("inf")
+    w[8, 0] = 60000.0
+    x[:, 0] = 60000.0  # products 3.6e9: fine in FP32, past FP16's range
+    s = f32(call_sums(x, w, path, F16))
+    _, _, s_ref = orc.linear(x, w, None, sums=True)
+    assert np.isnan(s[3]).all() and np.isnan(s_ref[3]).all()
+    assert eq_f32(s[:, 7], s_ref[:, 7]).all() and np.isinf(s[np.arange(40) != 3, 7]).all()
+    rows, cols = np.arange(40) != 3, np.arange(48) != 7
+    xc, wc = x.clone(), w.clone()
+    xc[3, 5], wc[7, 9] = 0.0, 0.0
+    S, A = orc.band(xc, wc)
+    ok, rep = tolerance.check_sums(s[rows][:, cols], S[rows][:, cols], A[rows][:, cols], 64)
+    assert ok.all(), rep
+    assert (np.abs(s[rows, 8]) > 1e9).all(), "FP32 sums must keep values past FP16's range"
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_sums_strided_output_with_guard_band(orc, path, dtype):
+    """FP32 output with a row stride that is not a multiple of 4 and a start that is
+    not 16-byte aligned (the element-wise store); nothing outside y is written."""
+    M, N, K = 67, 90, 200
+    x, w, _ = workloads.make_inputs(M, N, K, 0.07, seed=80, dtype=dtype)
+    _, _, s_ref = orc.linear(x, w, None, elem=elem_of(dtype), sums=True)
+    guard = torch.full((M + 2, 101), -7.25, dtype=torch.float32, device=DEV)
+    yv = guard[1:1 + M, 3:3 + N]
+    call_sums(x, w, path, dtype, out=yv)
+    g = f32(guard)
+    S, A = orc.band(x, w, elem=elem_of(dtype))
+    ok, rep = tolerance.check_sums(g[1:1 + M, 3:3 + N], S, A, K)
+    assert ok.all(), rep
+    mask = np.ones(g.shape, bool)
+    mask[1:1 + M, 3:3 + N] = False
+    assert (g[mask] == np.float32(-7.25)).all(), "wrote outside y"
+    # an aligned padded stride gives the same bits as the contiguous output
+    s0 = f32(call_sums(x, w, path, dtype))
+    ys = torch.zeros(M, N + 6, dtype=torch.float32, device=DEV)
+    call_sums(x, w, path, dtype, out=ys[:, :N])
+    assert np.array_equal(f32(ys[:, :N]).view(np.uint32), s0.view(np.uint32))
+    assert np.array_equal(g[1:1 + M, 3:3 + N].view(np.uint32), s0.view(np.uint32))
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bf16_strided_and_misaligned_operands_with_guard_band(orc, path):
+    M, N, K = 67, 90, 200
+    x, w, b = workloads.make_inputs(M, N, K, 0.07, seed=80, dtype=BF)
+    y_ref, p_ref = orc.linear(x, w, b, elem=tolerance.BF16)
+    xs = torch.full((M, 217), float("nan"), dtype=BF, device=DEV)
+    xv = xs[:, 1:1 + K]
+    xv.copy_(x.to(DEV))
+    ws = torch.full((N, 208), float("nan"), dtype=BF, device=DEV)
+    wv = ws[:, :K]
+    wv.copy_(w.to(DEV))
+    guard = torch.full((M + 2, 100), 12345.0, dtype=BF, device=DEV)
+    yv = guard[1:1 + M, 3:3 + N]
+    la.linear_bf16_ex(xv, wv, b.to(DEV), out=yv, path=path)
+    torch.cuda.synchronize()
+    g = words(guard)
+    S, A = orc.band(x, w, elem=tolerance.BF16)
+    ok, rep = tolerance.check_y(g[1:1 + M, 3:3 + N], y_ref, p_ref, A, elem=tolerance.BF16)
+    assert ok.all(), rep
+    sentinel = words(torch.tensor([12345.0], dtype=BF))[0]
+    mask = np.ones(g.shape, bool)
+    mask[1:1 + M, 3:3 + N] = False
+    assert (g[mask] == sentinel).all(), "wrote outside y"
+
+
+def test_bf16_paths_agree_on_exact_data(orc):
+    x, w, b = workloads.small_integers(40, 300, 700, seed=83, dtype=BF)
+    assert np.array_equal(words(call(x, w, b, la.PATH_GEMM, BF)), words(call(x, w, b, la.PATH_SKINNY, BF)))
+
+
+def test_dtype_errors_raise():
+    x = torch.zeros(4, 8, dtype=F16, device=DEV)
+    w = torch.zeros(6, 8, dtype=F16, device=DEV)
+    with pytest.raises(TypeError):
+        la.linear_bf16_nobias(x, w)
+    with pytest.raises(TypeError):
+        la.linear_f16_f32out(x, w, out=torch.zeros(4, 6, dtype=F16, device=DEV))

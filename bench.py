@@ -38,6 +38,11 @@ KERNEL_SOURCES = {
     "gemm_f16_stream": ["linear_amd/csrc/gemm_impl.h", "linear_amd/csrc/gemm_f16.hip",
                         "linear_amd/csrc/common.h"],
 }
+# substring of the demangled kernel name that each recorded kernel's counter rows carry
+KERNEL_PATTERNS = {
+    "skinny_f16_stream": "skinny_stream<8, 0, 0>",   # 8 waves, binary16, bias epilogue
+    "gemm_f16_stream": "gemm_stream<",
+}
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense FP16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 ROTATE_BYTES = 512 * 1024 * 1024
 
@@ -96,8 +101,8 @@ def record_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: 
         if not hits:
             raise SystemExit("no %s dispatches of %s under %s" % (counter, name, d))
         return hits[0]
-    kname, (fetch_kib, nf) = pick(fetch_dir, "FETCH_SIZE", kernel)
-    _, (write_kib, nw) = pick(write_dir, "WRITE_SIZE", kernel)
+    kname, (fetch_kib, nf) = pick(fetch_dir, "FETCH_SIZE", KERNEL_PATTERNS[kernel])
+    _, (write_kib, nw) = pick(write_dir, "WRITE_SIZE", KERNEL_PATTERNS[kernel])
     _, (cf_kib, _) = pick(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     _, (cw_kib, _) = pick(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     f_scale = COPYCAL_BYTES / (cf_kib * 1024.0)
@@ -381,7 +386,7 @@ def main():
                         "W [4096,4096], b [4096], fp16",
             "calls_per_step": launches,
             "weight_copies_rotated": detail["weight_copies"],
-            "kernel": "skinny_f16_stream (16 output columns x 16 rows per workgroup, 8 waves, "
+            "kernel": "skinny_stream<8, f16, bias> (16 output columns x 16 rows per workgroup, 8 waves, "
                       "v_mfma_f32_16x16x32_f16)",
         },
         "roofline": {

@@ -22,7 +22,7 @@ SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "skinny.hip", "linear_abi.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-fno-gpu-flush-denormals-to-zero",   # binary16 subnormals are kept (IEEE gradual underflow)

@@ -124,8 +124,31 @@ __device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // nearest even); with a bias, widen the rounded value and b[n] to FP32, add, and
 // round the sum to E.  FP32 mode: store the sums unrounded.  Columns past N are
 // skipped; rows are checked by the caller.
+// The bias words b[nb..nb+3] widened to FP32 (0 past N), for callers that load
+// them before their main loop so the load latency is off the kernel's tail.
+template <int E>
+__device__ inline f32x4 load_bias4(const LinearArgs& a, int nb) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (nb + e < a.N) ? widen<E>(a.b[nb + e]) : 0.f;
+    return r;
+}
+
+template <int E, int MODE>
+__device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, float v1, float v2, float v3,
+                              f32x4 bias);
+
 template <int E, int MODE>
 __device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, float v1, float v2, float v3) {
+    f32x4 bias = (f32x4){};
+    if (MODE == kOutBias) bias = load_bias4<E>(a, nb);
+    store4<E, MODE>(a, m, nb, v0, v1, v2, v3, bias);
+}
+
+// As above with the widened bias words already loaded (ignored unless MODE is kOutBias).
+template <int E, int MODE>
+__device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, float v1, float v2, float v3,
+                              f32x4 bias) {
     const float v[4] = {v0, v1, v2, v3};
     if (MODE == kOutF32) {
         float* dst = (float*)a.y + (int64_t)m * a.ldy + nb;
@@ -142,10 +165,7 @@ __device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, floa
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         uint16_t p = narrow<E>(v[e]);
-        if (MODE == kOutBias) {
-            const float bias = (nb + e < a.N) ? widen<E>(a.b[nb + e]) : 0.f;
-            p = narrow<E>(widen<E>(p) + bias);
-        }
+        if (MODE == kOutBias) p = narrow<E>(widen<E>(p) + bias[e]);
         o[e] = p;
     }
     uint16_t* dst = (uint16_t*)a.y + (int64_t)m * a.ldy + nb;

@@ -164,6 +164,31 @@ gemm_kernel(LinearArgs a) {
         }
 }
 
+// Calls f.template operator()<I>() for I = B .. N-1 (compile-time loop).
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < N) {
+        f.template operator()<B>();
+        static_for<B + 1, N>(f);
+    }
+}
+
+// Instruction order of one K step of the streaming GEMM: its first MFMA, the
+// NREAD fragment reads of the next step, then the other NMFMA - 1 MFMAs with ND
+// loads spaced evenly between them.
+template <int NMFMA, int NREAD, int ND>
+__device__ __forceinline__ void order_step() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NREAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+    constexpr int q = (NMFMA - 1) / (ND + 1);
+    static_for<0, ND>([&]<int d>() {
+        if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x008, q, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    });
+    if constexpr (NMFMA - 1 - q * ND > 0) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - 1 - q * ND, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // Streaming variant for 16-byte aligned layouts (x, weight 16-byte aligned, ldx,
 // ldw and K multiples of 8).
@@ -188,7 +213,7 @@ gemm_kernel(LinearArgs a) {
 // i.e. row l / CPR, stored chunk l % CPR, so it fetches the logical chunk that the
 // swizzle puts there.  With BK = 64 every load instruction covers whole 128-byte
 // rows.
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_stream(LinearArgs a) {
     constexpr int KS = BK / 16;                       // MFMA K steps per slice
@@ -236,17 +261,27 @@ gemm_stream(LinearArgs a) {
     }
 
     const int nk = (K + BK - 1) / BK;
-#define LIN_ISSUE(t_)                                                                    \
+    // One direct load: group j of this wave for slice t_ (j_ a compile-time index).
+#define LIN_ISSUE_ONE(t_, j_)                                                            \
     do {                                                                                 \
         const int t__ = (t_);                                                            \
         unsigned char* slot__ = smem + (t__ % STAGES) * SLICE;                           \
         const uint32_t kb__ = (uint32_t)(t__ * BK) * 2u;                                 \
-        _Pragma("unroll") for (int j = 0; j < GPW; ++j) {                                \
-            const int g = wave * GPW + j;                                                \
-            const bool kin__ = t__ * BK + gk[j] < K;                                     \
-            lds_dma16(g < BN / RPL ? rw : rx, slot__ + g * 1024, kin__ ? goff[j] + kb__ : kOOB); \
-        }                                                                                \
+        const int g__ = wave * GPW + (j_);                                               \
+        const bool kin__ = t__ * BK + gk[(j_)] < K;                                      \
+        lds_dma16(g__ < BN / RPL ? rw : rx, slot__ + g__ * 1024, kin__ ? goff[(j_)] + kb__ : kOOB); \
     } while (0)
+
+    // The loads of slice t + STAGES go into the slot that the barrier after slice
+    // t releases.  They are spread over a window of 1 + SP K steps (the last
+    // step of slice t and the first SP steps of slice t + 1), DPS per step, so
+    // that the CU's load requests trickle in between MFMAs instead of reaching the
+    // texture addresser as one burst that stalls every wave's instruction issue.
+    // (the window ends at least one K step before the barrier that waits for
+    // these loads: SPREAD is capped at KS - 2)
+    static_assert(SPREAD >= 0, "SPREAD counts K steps");
+    constexpr int SP = SPREAD < KS - 2 ? SPREAD : KS - 2;
+    constexpr int DPS = (GPW + SP) / (1 + SP);
 
     const int wn = wave % WN, wm = wave / WN;
     const int lr = lane & 31, lh = lane >> 5;
@@ -274,11 +309,15 @@ gemm_stream(LinearArgs a) {
 
     if (nk > 0) {
         // Requests past the last slice carry out-of-range offsets (zero fill, no
-        // memory traffic), so exactly STAGES - 1 slices are always in flight
-        // behind the one being waited for and every wait below is static.
+        // memory traffic), so the number of requests behind any slice is fixed and
+        // every wait below is static.  The prologue issues slices 0 .. STAGES-2 and
+        // the first DPS loads of slice STAGES-1, as the steady state would have.
 #pragma unroll
-        for (int t = 0; t < STAGES; ++t) LIN_ISSUE(t);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 1) * GPW) : "memory");
+        for (int t = 0; t < STAGES; ++t)
+#pragma unroll
+            for (int j = 0; j < GPW; ++j)
+                if (t + 1 < STAGES || j < DPS) LIN_ISSUE_ONE(t, j);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW + DPS) : "memory");
         __syncthreads();
 
         u32x4 af[2][FN], bf[2][FM];
@@ -300,45 +339,40 @@ gemm_stream(LinearArgs a) {
                 for (int j = 0; j < FM; ++j)
                     acc[i][j] = mfma32x32x16<E>(af[buf][i], bf[buf][j], acc[i][j]);
         };
-        // K steps 0 .. KS-2 of a slice: read the next step while this one multiplies
-        auto inner_steps = [&](const unsigned char* slot) {
-#pragma unroll
-            for (int ks = 0; ks + 1 < KS; ++ks) {
+        // K steps 0 .. KS-2 of slice t: read the next step while this one
+        // multiplies; the first SP steps also issue the deferred loads of
+        // slice t - 1 + STAGES
+        auto inner_steps = [&](int t) {
+            const unsigned char* slot = smem + (t % STAGES) * SLICE;
+            static_for<0, KS - 1>([&]<int ks>() {
                 read_frags(slot, ks + 1, (ks + 1) & 1);
                 mfmas(ks & 1);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - 1, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                constexpr int j0 = ks < SP ? DPS * (ks + 1) : GPW;
+                constexpr int j1 = ks < SP ? (DPS * (ks + 2) < GPW ? DPS * (ks + 2) : GPW) : GPW;
+                static_for<j0, j1>([&]<int j>() { LIN_ISSUE_ONE(t - 1 + STAGES, j); });
+                order_step<FN * FM, FN + FM, (j1 > j0 ? j1 - j0 : 0)>();
+            });
         };
 
         for (int t = 0; t + 1 < nk; ++t) {
-            const unsigned char* cur = smem + (t % STAGES) * SLICE;
-            inner_steps(cur);
-            // slice t + 1 has landed once only the STAGES - 2 later requests are
+            inner_steps(t);
+            // slice t + 1 has landed once only the later slices' requests are
             // outstanding; the barrier also waits for every wave's last reads of
             // slot t, which the refill below overwrites
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
             __syncthreads();
-            LIN_ISSUE(t + STAGES);
             read_frags(smem + ((t + 1) % STAGES) * SLICE, 0, KS & 1);
             mfmas((KS - 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
-#pragma unroll
-            for (int j = 0; j < GPW; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, FN * FM - GPW, 0);
-            __builtin_amdgcn_sched_barrier(0);
+            constexpr int D0 = DPS < GPW ? DPS : GPW;
+            static_for<0, D0>([&]<int j>() { LIN_ISSUE_ONE(t + STAGES, j); });
+            order_step<FN * FM, FN + FM, D0>();
         }
-        inner_steps(smem + ((nk - 1) % STAGES) * SLICE);
+        inner_steps(nk - 1);
         mfmas((KS - 1) & 1);
         // the zero-fill requests past the end must land before the LDS is released
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-#undef LIN_ISSUE
+#undef LIN_ISSUE_ONE
 
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -365,11 +399,11 @@ static const void* regstaged_fn(int mode) {
     return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutF32>;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD>
 static const void* stream_fn(int mode) {
-    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias>;
-    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound>;
-    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32>;
+    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD>;
+    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD>;
+    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD>;
 }
 
 static hipError_t launch(const void* fn, const LinearArgs& a, int threads, hipStream_t stream) {
@@ -390,11 +424,12 @@ hipError_t launch_gemm_t(int cfg, const LinearArgs& a, int mode, hipStream_t str
 template <int E>
 hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
     switch (cfg) {
-        case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E>(mode), a, 512, stream);
-        case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E>(mode), a, 512, stream);
-        case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E>(mode), a, 512, stream);
-        case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E>(mode), a, 256, stream);
-        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E>(mode), a, 256, stream);
+        // the load spread measured best on the two-slot 256 x 256 tile only
+        case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E, 1>(mode), a, 512, stream);
+        case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E, 0>(mode), a, 512, stream);
+        case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E, 0>(mode), a, 512, stream);
+        case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E, 0>(mode), a, 256, stream);
+        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E, 0>(mode), a, 256, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -26,6 +26,7 @@
 //    with the MFMAs, so every load is in flight at once), and consumes each weight
 //    fragment as it arrives.
 //  - skinny_kernel (any layout): element-wise masked loads of both operands.
+// Both request the bias words of the finishing wave before the main loop.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,6 +55,14 @@ skinny_stream(LinearArgs a) {
     const int ub = (int)((int64_t)wave * U / WAVES);
     const int ue = (int)((int64_t)(wave + 1) * U / WAVES);
     const int kend = min(ue * 32, K);
+
+    // wave 0 finishes the block: its bias words are requested now, ahead of the
+    // weight stream, so their latency is not added after the last weight byte lands
+    const int m = m0 + (lane & 15);
+    const int nb = n0 + (lane >> 4) * 4;
+    f32x4 bias = (f32x4){};
+    if (MODE == kOutBias && wave == 0) bias = load_bias4<E>(a, nb);
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc = (f32x4){};
     for (int u0 = ub; u0 < ue; u0 += PU) {
@@ -93,9 +102,7 @@ skinny_stream(LinearArgs a) {
     for (int w = 1; w < WAVES; ++w) s += red[w][lane];
 
     // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
-    const int m = m0 + (lane & 15);
-    const int nb = n0 + (lane >> 4) * 4;
-    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3]);
+    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
 }
 
 template <int WAVES, int E, int MODE>
@@ -116,6 +123,11 @@ skinny_kernel(LinearArgs a) {
     const int U = (K + 31) / 32;
     const int ub = (int)((int64_t)wave * U / WAVES);
     const int ue = (int)((int64_t)(wave + 1) * U / WAVES);
+
+    const int m = m0 + (lane & 15);
+    const int nb = n0 + (lane >> 4) * 4;
+    f32x4 bias = (f32x4){};
+    if (MODE == kOutBias && wave == 0) bias = load_bias4<E>(a, nb);
 
     f32x4 acc = (f32x4){};
     for (int u = ub; u < ue; u += UNROLL) {
@@ -141,9 +153,7 @@ skinny_kernel(LinearArgs a) {
     for (int w = 1; w < WAVES; ++w) s += red[w][lane];
 
     // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
-    const int m = m0 + (lane & 15);
-    const int nb = n0 + (lane >> 4) * 4;
-    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3]);
+    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
 }
 
 template <int E>

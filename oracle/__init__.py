@@ -75,6 +75,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_band.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _i64, _i64, _i64, _f64p, _f64p,
                                 ctypes.c_int]
     lib.oracle_band.restype = ctypes.c_int
+    lib.oracle_f64_to_elem.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_f64_to_elem.restype = ctypes.c_uint16
+    _i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_epilogue.argtypes = [ctypes.c_int, _i32p, ctypes.c_int, _u16p, _u16p, _u16p, _u16p, _u16p, _i64]
+    lib.oracle_epilogue.restype = None
+    lib.oracle_unary_array.argtypes = [ctypes.c_int, ctypes.c_int, _u16p, _u16p, _i64]
+    lib.oracle_unary_array.restype = None
     lib.oracle_bf16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
     lib.oracle_bf16_to_f32_array.restype = None
     lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
@@ -109,6 +116,16 @@ def _ptr(a: np.ndarray, ctype):
 
 F16 = 0
 BF16 = 1
+
+# Epilogue steps ("The Graph IR", op table: ContractionEpilogue)
+EPI_BIAS = 1
+EPI_RESIDUAL = 2
+EPI_MUL = 3
+EPI_SILU = 4
+EPI_GELU_TANH = 5
+EPI_GELU_ERF = 6
+UNARY_EXP = 7
+UNARY_ERF = 8
 
 
 def _as_words(a) -> np.ndarray:
@@ -231,6 +248,42 @@ class Oracle:
         if rc != 0:
             raise MemoryError("oracle_band_f64 failed")
         return S, A
+
+    # -- multi-step epilogue ------------------------------------------------------
+    def f64_to_elem(self, v, elem: int = F16) -> np.ndarray:
+        v = np.asarray(v, np.float64)
+        out = np.empty(v.shape, np.uint16)
+        flat = v.ravel()
+        o = out.ravel()
+        for i in range(flat.size):
+            o[i] = self.lib.oracle_f64_to_elem(int(elem), float(flat[i]))
+        return out
+
+    def unary(self, op: int, x, elem: int = F16) -> np.ndarray:
+        """An activation (EPI_SILU, EPI_GELU_TANH, EPI_GELU_ERF) or a rounded primitive
+        (UNARY_EXP, UNARY_ERF) over element-type words."""
+        x = _as_words(x)
+        out = np.empty(x.shape, np.uint16)
+        self.lib.oracle_unary_array(int(elem), int(op), _ptr(x, ctypes.c_uint16), _ptr(out, ctypes.c_uint16), x.size)
+        return out
+
+    def epilogue(self, ops, t, bias=None, res=None, mul=None, elem: int = F16) -> np.ndarray:
+        """The steps `ops` applied to element-type words t (any shape); bias, res and
+        mul are per-element words of t's shape (broadcast by the caller) or None."""
+        t = _as_words(t)
+        opsa = np.ascontiguousarray(ops, dtype=np.int32)
+        def opt(a):
+            if a is None:
+                return None, None
+            a = np.ascontiguousarray(np.broadcast_to(_as_words(a), t.shape))
+            return a, _ptr(a, ctypes.c_uint16)
+        bk, bp = opt(bias)
+        rk, rp = opt(res)
+        mk, mp = opt(mul)
+        out = np.empty(t.shape, np.uint16)
+        self.lib.oracle_epilogue(int(elem), opsa.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(opsa.size),
+                                 _ptr(t, ctypes.c_uint16), bp, rp, mp, _ptr(out, ctypes.c_uint16), t.size)
+        return out
 
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())

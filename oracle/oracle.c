@@ -23,7 +23,10 @@
  * The same definition with bfloat16 operands ("The Graph IR", op table: a Cast
  * to bf16 rounds to bf16 precision; ContractionEpilogue: a BF16 head rounds to
  * BF16 before the first epilogue step reads it) and the unrounded FP32 sum (the op
- * table's DenseContraction produces f32) are provided too.
+ * table's DenseContraction produces f32) are provided too, and so is the
+ * multi-step contraction epilogue (bias, residual, multiply, SiLU and GeLU
+ * compositions, each primitive rounding through the element type; at the end of
+ * this file).
  *
  * Readings where the pages are silent (all listed in the design notes):
  *   - "rounded to FP16" is IEEE roundTiesToEven, with gradual underflow
@@ -348,4 +351,147 @@ int oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ---------------------------------------------------------------------------
+ * Multi-step contraction epilogue ("The Graph IR", op table: ContractionEpilogue).
+ *
+ * The head contraction's result keeps the head dtype (binary16 or bfloat16: the
+ * projection is rounded to it first) and every epilogue step rounds through
+ * that dtype.  The steps are pointwise primitives of the op table (Binary Add /
+ * Mul / Div, Unary Neg / Exp / Erf) over the element type; the activations are
+ * the compositions the "Tracing a Model" page describes for the feed-forward:
+ *
+ *   SiLU        x / (1 + exp(-x))                    over Neg, Exp, Add, Div
+ *   GeLU, tanh  x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3)))   the same
+ *               sigmoid form over Mul, Add, Exp and Div
+ *   GeLU, erf   (x (1 + erf(x / sqrt 2))) * 0.5       over Mul, Erf, Add
+ *
+ * Readings (the pages name the primitives, not their precision):
+ *   - each primitive returns its exact result rounded to the element type
+ *     (round to nearest, ties to even): the operands are widened exactly to
+ *     double, the operation is carried out in double, and the double is rounded
+ *     to the element type.  For +, -, *, / double has more than 2p+2 bits, so
+ *     rounding through double equals one correct rounding; for exp and erf the
+ *     double result is within an ulp of double, far inside the element type's
+ *     grid (the pins check every element-type input against a high-precision
+ *     evaluation);
+ *   - constants (1, 0.5, 0.044715, -2 sqrt(2/pi), 1/sqrt 2) are element-type
+ *     values: their real value rounded to the element type;
+ *   - the evaluation order inside a composition is the one written above, left
+ *     to right (x^3 as (x*x)*x, the constant multiplied last).
+ * ------------------------------------------------------------------------- */
+#define ORACLE_EPI_BIAS 1       /* t + b[n]                 */
+#define ORACLE_EPI_RESIDUAL 2   /* t + r[m, n]              */
+#define ORACLE_EPI_MUL 3        /* t * u[m, n]              */
+#define ORACLE_EPI_SILU 4
+#define ORACLE_EPI_GELU_TANH 5
+#define ORACLE_EPI_GELU_ERF 6
+
+/* Round a double to the element type, ties to even: snap to the type's grid at
+   the value's binade with nearbyint (default rounding mode), then encode the
+   now exactly representable value through the FP32 encoders above. */
+uint16_t oracle_f64_to_elem(int elem, double v) {
+    if (isnan(v)) return elem ? 0x7fc0u : 0x7e00u;
+    if (isinf(v)) return (uint16_t)((v < 0 ? 0x8000u : 0u) | (elem ? 0x7f80u : 0x7c00u));
+    const int p = elem ? 8 : 11;                 /* significand bits */
+    const int emin = elem ? -126 : -14;          /* smallest normal exponent */
+    const double maxv = elem ? ldexp(2.0 - ldexp(1.0, -7), 127) : 65504.0;
+    double a = fabs(v);
+    double r;
+    if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int e;
+        frexp(a, &e);                            /* a = f * 2^e, f in [0.5, 1) */
+        e -= 1;                                  /* a in [2^e, 2^(e+1)) */
+        if (e < emin) e = emin;                  /* subnormal grid */
+        const double q = ldexp(1.0, e - (p - 1));
+        r = nearbyint(a / q) * q;
+    }
+    uint16_t bits;
+    if (r > maxv) bits = elem ? 0x7f80u : 0x7c00u;
+    else bits = elem ? oracle_f32_to_bf16((float)r) : oracle_f32_to_f16((float)r);
+    if (signbit(v)) bits |= 0x8000u;
+    return bits;
+}
+
+static double wd(int elem, uint16_t h) { return (double)widen16(elem, h); }
+static uint16_t rd(int elem, double v) { return oracle_f64_to_elem(elem, v); }
+
+/* Element-type constants, rounded from their real values. */
+static uint16_t cst(int elem, double v) { return rd(elem, v); }
+
+uint16_t oracle_epi_silu(int elem, uint16_t x) {
+    uint16_t n = rd(elem, -wd(elem, x));
+    uint16_t e = rd(elem, exp(wd(elem, n)));
+    uint16_t d = rd(elem, wd(elem, cst(elem, 1.0)) + wd(elem, e));
+    return rd(elem, wd(elem, x) / wd(elem, d));
+}
+
+uint16_t oracle_epi_gelu_tanh(int elem, uint16_t x) {
+    const uint16_t c1 = cst(elem, 0.044715);
+    const uint16_t c2 = cst(elem, -2.0 * sqrt(2.0 / 3.14159265358979323846));
+    uint16_t a = rd(elem, wd(elem, x) * wd(elem, x));
+    uint16_t b = rd(elem, wd(elem, a) * wd(elem, x));
+    uint16_t c = rd(elem, wd(elem, b) * wd(elem, c1));
+    uint16_t d = rd(elem, wd(elem, x) + wd(elem, c));
+    uint16_t z = rd(elem, wd(elem, d) * wd(elem, c2));
+    uint16_t e = rd(elem, exp(wd(elem, z)));
+    uint16_t f = rd(elem, wd(elem, cst(elem, 1.0)) + wd(elem, e));
+    return rd(elem, wd(elem, x) / wd(elem, f));
+}
+
+uint16_t oracle_epi_gelu_erf(int elem, uint16_t x) {
+    const uint16_t c3 = cst(elem, 0.70710678118654752440);
+    uint16_t s = rd(elem, wd(elem, x) * wd(elem, c3));
+    uint16_t f = rd(elem, erf(wd(elem, s)));
+    uint16_t g = rd(elem, wd(elem, cst(elem, 1.0)) + wd(elem, f));
+    uint16_t h = rd(elem, wd(elem, x) * wd(elem, g));
+    return rd(elem, wd(elem, h) * wd(elem, cst(elem, 0.5)));
+}
+
+/* Unary primitives rounded to the element type (pinned one by one). */
+uint16_t oracle_epi_exp(int elem, uint16_t x) { return rd(elem, exp(wd(elem, x))); }
+uint16_t oracle_epi_erf(int elem, uint16_t x) { return rd(elem, erf(wd(elem, x))); }
+
+/* One step applied to t (an element-type word). */
+static uint16_t epi_step(int elem, int op, uint16_t t, uint16_t bias, uint16_t res, uint16_t mul) {
+    switch (op) {
+        case ORACLE_EPI_BIAS: return rd(elem, wd(elem, t) + wd(elem, bias));
+        case ORACLE_EPI_RESIDUAL: return rd(elem, wd(elem, t) + wd(elem, res));
+        case ORACLE_EPI_MUL: return rd(elem, wd(elem, t) * wd(elem, mul));
+        case ORACLE_EPI_SILU: return oracle_epi_silu(elem, t);
+        case ORACLE_EPI_GELU_TANH: return oracle_epi_gelu_tanh(elem, t);
+        case ORACLE_EPI_GELU_ERF: return oracle_epi_gelu_erf(elem, t);
+        default: return t;
+    }
+}
+
+/*
+ * The epilogue over element-type words t[i] (i < count): out[i] = the steps
+ * ops[0 .. nsteps-1] applied in order to t[i], with the extra inputs of element
+ * i at bias[i], res[i], mul[i] (arrays of count words; NULL when no step reads
+ * them).  Callers gather the broadcast bias and the [M, N] inputs per element.
+ */
+void oracle_epilogue(int elem, const int32_t* ops, int nsteps, const uint16_t* t, const uint16_t* bias,
+                     const uint16_t* res, const uint16_t* mul, uint16_t* out, int64_t count) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        uint16_t v = t[i];
+        for (int s = 0; s < nsteps; ++s)
+            v = epi_step(elem, ops[s], v, bias ? bias[i] : 0, res ? res[i] : 0, mul ? mul[i] : 0);
+        out[i] = v;
+    }
+}
+
+/* Element-wise unary primitive over an array (op: ORACLE_EPI_SILU .. GELU_ERF, or
+   7 = exp, 8 = erf). */
+void oracle_unary_array(int elem, int op, const uint16_t* x, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        if (op == 7) out[i] = oracle_epi_exp(elem, x[i]);
+        else if (op == 8) out[i] = oracle_epi_erf(elem, x[i]);
+        else out[i] = epi_step(elem, op, x[i], 0, 0, 0);
+    }
 }

@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import pins
+import pins_epilogue
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -54,6 +55,33 @@ MUTANTS = [
     ("sums_before_accumulate", "if (y32) y32[m * ldy + n] = acc;", "if (y32) y32[m * ldy + n] = acc * 1.0000001f;"),
 ]
 
+# Mistakes in the multi-step epilogue, caught by the epilogue pins.
+EPI_MUTANTS = [
+    ("epi_silu_exp_sign", "uint16_t e = rd(elem, exp(wd(elem, n)));", "uint16_t e = rd(elem, exp(wd(elem, x)));"),
+    ("epi_silu_unrounded_exp",
+     "uint16_t d = rd(elem, wd(elem, cst(elem, 1.0)) + wd(elem, e));\n    return rd(elem, wd(elem, x) / wd(elem, d));",
+     "uint16_t d = rd(elem, 1.0 + exp(-wd(elem, x))); (void)e;\n    return rd(elem, wd(elem, x) / wd(elem, d));"),
+    ("epi_silu_one_rounding", "    return rd(elem, wd(elem, x) / wd(elem, d));\n}\n\nuint16_t oracle_epi_gelu_tanh",
+     "    (void)d; return rd(elem, wd(elem, x) / (1.0 + exp(-wd(elem, x))));\n}\n\nuint16_t oracle_epi_gelu_tanh"),
+    ("epi_gelu_cubic_coeff", "const uint16_t c1 = cst(elem, 0.044715);", "const uint16_t c1 = cst(elem, 0.44715);"),
+    ("epi_gelu_square_not_cube", "uint16_t b = rd(elem, wd(elem, a) * wd(elem, x));", "uint16_t b = a;"),
+    ("epi_gelu_tanh_unrounded_z", "uint16_t e = rd(elem, exp(wd(elem, z)));",
+     "uint16_t e = rd(elem, exp(wd(elem, d) * -2.0 * sqrt(2.0 / 3.14159265358979323846))); (void)z;"),
+    ("epi_gelu_erf_no_half", "return rd(elem, wd(elem, h) * wd(elem, cst(elem, 0.5)));", "return h;"),
+    ("epi_gelu_erf_no_rsqrt2", "const uint16_t c3 = cst(elem, 0.70710678118654752440);",
+     "const uint16_t c3 = cst(elem, 1.0);"),
+    ("epi_gelu_erf_as_tanh", "uint16_t f = rd(elem, erf(wd(elem, s)));", "uint16_t f = rd(elem, tanh(wd(elem, s)));"),
+    ("epi_residual_reads_bias", "case ORACLE_EPI_RESIDUAL: return rd(elem, wd(elem, t) + wd(elem, res));",
+     "case ORACLE_EPI_RESIDUAL: return rd(elem, wd(elem, t) + wd(elem, bias));"),
+    ("epi_mul_as_add", "case ORACLE_EPI_MUL: return rd(elem, wd(elem, t) * wd(elem, mul));",
+     "case ORACLE_EPI_MUL: return rd(elem, wd(elem, t) + wd(elem, mul));"),
+    ("epi_steps_reversed", "for (int s = 0; s < nsteps; ++s)\n            v = epi_step(elem, ops[s],",
+     "for (int s = nsteps - 1; s >= 0; --s)\n            v = epi_step(elem, ops[s],"),
+    ("epi_round_ties_away", "r = nearbyint(a / q) * q;", "r = round(a / q) * q;"),
+    ("epi_round_no_subnormal_grid", "if (e < emin) e = emin;                  /* subnormal grid */", ""),
+    ("epi_round_max_overflows", "if (r > maxv) bits = elem ? 0x7f80u : 0x7c00u;", "if (r >= maxv) bits = elem ? 0x7f80u : 0x7c00u;"),
+]
+
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(tmp_path, name, old, new):
@@ -72,3 +100,22 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
             caught.append(pin.__name__)
             break
     assert caught, "no pin catches mutant " + name
+
+
+@pytest.mark.parametrize("name,old,new", EPI_MUTANTS, ids=[m[0] for m in EPI_MUTANTS])
+def test_epilogue_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site vanished: " + name
+    mutated = src.replace(old, new, 1)
+    path = str(tmp_path / ("m_%s.c" % name))
+    open(path, "w").write(mutated)
+    lib = oracle.build(src=path, out=str(tmp_path / ("lib_%s.so" % name)))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in pins_epilogue.EPILOGUE_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, "no epilogue pin catches mutant " + name

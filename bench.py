@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
-    ap.add_argument("--variant", default="f16", help="with --only: f16, bf16, f16_f32out or bf16_f32out")
+    ap.add_argument("--variant", default="f16", help="with --only: f16, bf16, f16_f32out, bf16_f32out or "
+                    "<f16|bf16>_epi_<gelu|res|silu_mul|silu>")
     ap.add_argument("--no-variants", action="store_true", help="skip the bfloat16 / FP32-output timings")
     ap.add_argument("--record-traffic", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR"),
@@ -210,15 +211,32 @@ def bench_decode(args, torch, la, workloads, stream, dtype=None):
     return ms, detail
 
 
+# epilogue programs timed by the bench: name -> (steps, reads a residual, reads a gate input)
+EPI_PROGRAMS = {
+    "gelu": ("EPI_BIAS EPI_GELU_TANH", False, False),
+    "res": ("EPI_BIAS EPI_RESIDUAL", True, False),
+    "silu_mul": ("EPI_SILU EPI_MUL", False, True),
+    "silu": ("EPI_BIAS EPI_SILU", False, False),
+}
+
+
 def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
-    """One prefill shape.  variant: "f16" (the layer), "bf16" (bfloat16 layer) or
-    "f16_f32out" / "bf16_f32out" (the unrounded FP32 sums, no bias)."""
+    """One prefill shape.  variant: "f16" (the layer), "bf16" (bfloat16 layer),
+    "f16_f32out" / "bf16_f32out" (the unrounded FP32 sums, no bias) or
+    "<f16|bf16>_epi_<program>" (an epilogue program of EPI_PROGRAMS)."""
     wl = workloads.WORKLOADS[name]
     dtype = torch.bfloat16 if variant.startswith("bf16") else torch.float16
     sums = variant.endswith("f32out")
+    prog = variant.split("_epi_", 1)[1] if "_epi_" in variant else None
     x, w, b = workloads.workload_inputs(name, seed=0, device="cuda", dtype=dtype)
-    # algorithmic bytes: FP32 output is 4 B per element and there is no bias
+    # algorithmic bytes: FP32 output is 4 B per element and there is no bias; an
+    # epilogue reads its [M, N] inputs once (2 B per element each)
     nbytes = wl.bytes + (2 * wl.M * wl.N - 2 * wl.N if sums else 0)
+    ops, r_in, u_in = [], False, False
+    if prog:
+        names, r_in, u_in = EPI_PROGRAMS[prog]
+        ops = [getattr(la, n) for n in names.split()]
+        nbytes += 2 * wl.M * wl.N * (int(r_in) + int(u_in)) - (0 if la.EPI_BIAS in ops else 2 * wl.N)
     sets = rotation_sets(nbytes)
     xs = [x] + [x.clone() for _ in range(sets - 1)]
     ws = [w] + [w.clone() for _ in range(sets - 1)]
@@ -226,13 +244,24 @@ def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
           for _ in range(sets)]
     if sums:
         fn = la.linear_bf16_f32out if dtype == torch.bfloat16 else la.linear_f16_f32out
+    elif prog:
+        fn = la.linear_bf16_epilogue if dtype == torch.bfloat16 else la.linear_f16_epilogue
     else:
         fn = la.linear_bf16 if dtype == torch.bfloat16 else la.linear_f16
+    g = torch.Generator(device="cpu").manual_seed(1)
+    rs = [torch.randn(wl.M, wl.N, generator=g).to(dtype).to("cuda") for _ in range(sets)] if r_in else None
+    us = [torch.rand(wl.M, wl.N, generator=g).to(dtype).to("cuda") for _ in range(sets)] if u_in else None
+    if prog:   # builds the activation tables outside the capture
+        fn(xs[0], ws[0], ops, bias=b, residual=rs[0] if rs else None, mul=us[0] if us else None, out=ys[0])
+        torch.cuda.synchronize()
 
     def call(i):
         k = i % sets
         if sums:
             fn(xs[k], ws[k], out=ys[k], stream=stream)
+        elif prog:
+            fn(xs[k], ws[k], ops, bias=b, residual=rs[k] if rs else None, mul=us[k] if us else None, out=ys[k],
+               stream=stream)
         else:
             fn(xs[k], ws[k], b, out=ys[k], stream=stream)
 
@@ -244,7 +273,7 @@ def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
     del graph
     tflops = wl.flops / (ms * 1e-3) / 1e12
     plan = la.linear_f16_plan(x, w, b)
-    del xs, ws, ys
+    del xs, ws, ys, rs, us
     return {
         "M": wl.M, "N": wl.N, "K": wl.K, "variant": variant,
         "us_per_call": round(ms * 1e3, 3),
@@ -357,7 +386,9 @@ def main():
         log("decode bf16", json.dumps(variants["decode_bf16"]))
         if not args.no_prefill:
             for name, calls, var in (("attn", 50, "bf16"), ("attn", 50, "f16_f32out"),
-                                     ("attn", 50, "bf16_f32out"), ("down", 50, "bf16")):
+                                     ("attn", 50, "bf16_f32out"), ("down", 50, "bf16"),
+                                     ("mlp_up", 30, "f16_epi_gelu"), ("down", 50, "f16_epi_res"),
+                                     ("attn", 50, "f16_epi_silu_mul"), ("gemv16", 400, "f16_epi_silu")):
                 variants["%s_%s" % (name, var)] = r = bench_gemm(name, torch, la, workloads, stream, calls, var)
                 log(json.dumps(r))
     torch.cuda.synchronize()

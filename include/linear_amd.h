@@ -56,6 +56,8 @@ extern "C" {
 #define LINEAR_E_PATH     5  /* unknown path selector */
 #define LINEAR_E_DEVICE   6  /* no usable gfx950 device current, or a HIP query failed */
 #define LINEAR_E_LAUNCH   7  /* a kernel launch failed; linear_last_hip_error() has the HIP code */
+#define LINEAR_E_EPILOGUE 8  /* epilogue program: step count outside 0..LINEAR_EPI_MAX_STEPS or an unknown step */
+#define LINEAR_E_CAPTURE  9  /* the first activation epilogue on a device was called under stream capture */
 
 /* Path selectors for linear_f16_ex / linear_f16_plan. */
 #define LINEAR_PATH_AUTO   0  /* M <= 16: skinny path; otherwise the MFMA tiled GEMM */
@@ -147,6 +149,74 @@ int32_t linear_bf16_f32out(const uint16_t* x, int64_t ldx,
                            float* y, int64_t ldy,
                            int64_t M, int64_t N, int64_t K,
                            int32_t path, void* stream);
+
+/*
+ * Multi-step contraction epilogue ("The Graph IR", op table: ContractionEpilogue,
+ * whose extra inputs are the bias, a residual and so on: the head contraction's
+ * result keeps its dtype and every step rounds through it), with the activation
+ * compositions of "Tracing a Model" (the gated feed-forward section: SiLU as
+ * x / (1 + exp(-x)) over Neg, Exp, Add and Div; the tanh GeLU in the same
+ * sigmoid form, x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3))); the exact GeLU
+ * (x (1 + erf(x / sqrt 2))) * 0.5 on the Erf primitive).
+ *
+ *     t = RNE_E( sum_k x[m,k] * weight[n,k] )          the projection, as linear_*_nobias
+ *     for each step s: t = step_s(t)                    each result rounded to E
+ *     y[m,n] = t
+ *
+ * Steps (op[s]):
+ *   LINEAR_EPI_BIAS       t + bias[n]
+ *   LINEAR_EPI_RESIDUAL   t + residual[m * ldr + n]
+ *   LINEAR_EPI_MUL        t * mul[m * ldm + n]     (the gate product of a gated feed-forward)
+ *   LINEAR_EPI_SILU, LINEAR_EPI_GELU_TANH, LINEAR_EPI_GELU_ERF
+ * Every primitive of a step (each Add, Mul, Div, Neg, Exp, Erf of a composition,
+ * left to right, x^3 as (x*x)*x) returns its exact result rounded to E, round to
+ * nearest even; the constants 1, 0.5, 0.044715, -2 sqrt(2/pi) and 1/sqrt 2 are
+ * E values (their real value rounded to E).  IEEE special values propagate
+ * (e.g. SiLU of -inf is NaN: -inf / inf).
+ *
+ * bias, residual and mul are device words of the call's element type, caller
+ * owned; each is read only by the steps that name it and may be NULL otherwise.
+ * y may be the residual itself (same pointer, ldr == ldy: y = ... + y in place);
+ * any other overlap of y with an input is LINEAR_E_ALIAS.  The program is read
+ * when the call is made (the struct may be reused right after the call returns).
+ * The activation steps use tables the library builds on the device at the first
+ * such call per device and element type: that call waits for the build on
+ * `stream`, and made under stream capture it returns LINEAR_E_CAPTURE with
+ * nothing enqueued.  With no steps the call is linear_*_nobias; with the single
+ * step LINEAR_EPI_BIAS it gives the bits of linear_*.
+ */
+#define LINEAR_EPI_MAX_STEPS 8
+#define LINEAR_EPI_BIAS      1
+#define LINEAR_EPI_RESIDUAL  2
+#define LINEAR_EPI_MUL       3
+#define LINEAR_EPI_SILU      4
+#define LINEAR_EPI_GELU_TANH 5
+#define LINEAR_EPI_GELU_ERF  6
+
+typedef struct linear_epilogue {
+    int32_t nsteps;                        /* 0 .. LINEAR_EPI_MAX_STEPS */
+    int32_t op[LINEAR_EPI_MAX_STEPS];      /* LINEAR_EPI_*, applied in index order */
+    const uint16_t* bias;                  /* [N] */
+    const uint16_t* residual;              /* [M, N], row stride ldr >= N */
+    int64_t ldr;
+    const uint16_t* mul;                   /* [M, N], row stride ldm >= N */
+    int64_t ldm;
+} linear_epilogue;
+
+int32_t linear_f16_epilogue(const uint16_t* x, int64_t ldx,
+                            const uint16_t* weight, int64_t ldw,
+                            const linear_epilogue* epilogue,
+                            uint16_t* y, int64_t ldy,
+                            int64_t M, int64_t N, int64_t K,
+                            int32_t path, void* stream);
+
+/* The same with bfloat16 x, weight, epilogue inputs and y. */
+int32_t linear_bf16_epilogue(const uint16_t* x, int64_t ldx,
+                             const uint16_t* weight, int64_t ldw,
+                             const linear_epilogue* epilogue,
+                             uint16_t* y, int64_t ldy,
+                             int64_t M, int64_t N, int64_t K,
+                             int32_t path, void* stream);
 
 /* Which kernel a call would launch.  Pure host function: touches no device. */
 typedef struct linear_plan {

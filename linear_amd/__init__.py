@@ -24,6 +24,17 @@ LINEAR_E_ALIAS = 4
 LINEAR_E_PATH = 5
 LINEAR_E_DEVICE = 6
 LINEAR_E_LAUNCH = 7
+LINEAR_E_EPILOGUE = 8
+LINEAR_E_CAPTURE = 9
+
+# Epilogue steps (include/linear_amd.h, LINEAR_EPI_*)
+EPI_MAX_STEPS = 8
+EPI_BIAS = 1
+EPI_RESIDUAL = 2
+EPI_MUL = 3
+EPI_SILU = 4
+EPI_GELU_TANH = 5
+EPI_GELU_ERF = 6
 
 PATH_AUTO = 0
 PATH_GEMM = 1
@@ -31,6 +42,7 @@ PATH_SKINNY = 2
 
 ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_f32out",
                 "linear_bf16", "linear_bf16_nobias", "linear_bf16_ex", "linear_bf16_f32out",
+                "linear_f16_epilogue", "linear_bf16_epilogue",
                 "linear_f16_plan", "linear_status_string", "linear_last_hip_error")
 
 
@@ -51,6 +63,12 @@ class _Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32), ("vector_io", ctypes.c_int32),
                 ("grid", ctypes.c_int64)]
+
+
+class _Epilogue(ctypes.Structure):
+    _fields_ = [("nsteps", ctypes.c_int32), ("op", ctypes.c_int32 * EPI_MAX_STEPS),
+                ("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p), ("ldr", ctypes.c_int64),
+                ("mul", ctypes.c_void_p), ("ldm", ctypes.c_int64)]
 
 
 _LIB = None
@@ -81,6 +99,9 @@ def _lib():
     lib.linear_bf16_ex.restype = i32
     for name in ("linear_f16_f32out", "linear_bf16_f32out"):
         getattr(lib, name).argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, vp]
+        getattr(lib, name).restype = i32
+    for name in ("linear_f16_epilogue", "linear_bf16_epilogue"):
+        getattr(lib, name).argtypes = [vp, i64, vp, i64, ctypes.POINTER(_Epilogue), vp, i64, i64, i64, i64, i32, vp]
         getattr(lib, name).restype = i32
     lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
                                     ctypes.POINTER(_Plan)]
@@ -225,6 +246,48 @@ def linear_bf16_f32out(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor 
     rc = _lib().linear_bf16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
     _check(rc, "linear_bf16_f32out")
     return out
+
+
+def _epilogue_call(fn_name, dtype, x, weight, ops, bias, residual, mul, out, path, stream):
+    ops = [int(o) for o in ops]
+    if len(ops) > EPI_MAX_STEPS:
+        raise ValueError("at most %d epilogue steps" % EPI_MAX_STEPS)
+    xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, dtype)
+    ep = _Epilogue()
+    ep.nsteps = len(ops)
+    for i, o in enumerate(ops):
+        ep.op[i] = o
+    if bias is not None:
+        if bias.dtype != dtype or bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous %s [N] tensor" % dtype)
+        ep.bias = bias.data_ptr()
+    for name, t in (("residual", residual), ("mul", mul)):
+        if t is None:
+            continue
+        tp, ld = _mat(t, name, dtype)
+        if tuple(t.shape) != (M, N):
+            raise ValueError("%s must be [%d, %d]" % (name, M, N))
+        setattr(ep, name, tp)
+        setattr(ep, "ldr" if name == "residual" else "ldm", ld)
+    rc = getattr(_lib(), fn_name)(xp, ldx, wp, ldw, ctypes.byref(ep), yp, ldy, M, N, K, int(path),
+                                  _stream_handle(stream, x, out))
+    _check(rc, fn_name)
+    return out
+
+
+def linear_f16_epilogue(x: torch.Tensor, weight: torch.Tensor, ops, bias=None, residual=None, mul=None,
+                        out: torch.Tensor | None = None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """The projection followed by the epilogue steps `ops` (EPI_*), each rounded to binary16.
+    bias [N], residual and mul [M, N] as the steps need them; out may be the residual itself."""
+    return _epilogue_call("linear_f16_epilogue", torch.float16, x, weight, ops, bias, residual, mul, out, path,
+                          stream)
+
+
+def linear_bf16_epilogue(x: torch.Tensor, weight: torch.Tensor, ops, bias=None, residual=None, mul=None,
+                         out: torch.Tensor | None = None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """linear_f16_epilogue on bfloat16 operands, inputs and output."""
+    return _epilogue_call("linear_bf16_epilogue", torch.bfloat16, x, weight, ops, bias, residual, mul, out, path,
+                          stream)
 
 
 def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,

@@ -15,6 +15,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// The steps of a multi-step contraction epilogue, applied in order to the
+// rounded projection, each result rounded to the element type.
+constexpr int kEpiMaxSteps = 8;
+enum : int { kEpiBias = 1, kEpiResidual = 2, kEpiMul = 3, kEpiSilu = 4, kEpiGeluTanh = 5, kEpiGeluErf = 6 };
+constexpr int kActWords = 65536;   // one table entry per 16-bit input word
+
+struct EpiArgs {
+    const uint16_t* bias;   // [N]
+    const uint16_t* res;    // [M, N], row stride ldr
+    const uint16_t* mul;    // [M, N], row stride ldm
+    const uint16_t* act;    // this element type's tables: SiLU, tanh GeLU, erf GeLU (3 x kActWords)
+    int64_t ldr, ldm;
+    int nsteps;
+    uint8_t ops[kEpiMaxSteps];
+    int vec16;              // bits: 1 y, 2 bias, 4 res, 8 mul allow 16-byte (8-word) accesses
+};
+
 // Arguments of one linear-layer launch.  Pointers are device pointers to 16-bit
 // words (binary16 or bfloat16, per the kernel's element type); y holds 16-bit
 // words or, in the FP32-output mode, floats.  Strides in elements.
@@ -27,14 +44,16 @@ struct LinearArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int vec_store;       // 1: y aligned for 4-element vector stores and ldy % 4 == 0
+    EpiArgs epi;         // the epilogue program (kOutEpi only)
 };
 
 // Element types of x, weight, b and (rounded) y.
 enum : int { kF16 = 0, kBF16 = 1 };
 
 // Output modes: round the FP32 sum to the element type and add the bias (then
-// round again); round only; or store the FP32 sum itself.
-enum : int { kOutBias = 0, kOutRound = 1, kOutF32 = 2 };
+// round again); round only; store the FP32 sum itself; or round and run the
+// epilogue program of a.epi.
+enum : int { kOutBias = 0, kOutRound = 1, kOutF32 = 2, kOutEpi = 3 };
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, no stride.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -124,6 +143,134 @@ __device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // nearest even); with a bias, widen the rounded value and b[n] to FP32, add, and
 // round the sum to E.  FP32 mode: store the sums unrounded.  Columns past N are
 // skipped; rows are checked by the caller.
+// The epilogue program on one rounded projection word t at (m, n).  Additions and
+// the multiply run in FP32 on exactly widened operands and round to E once: FP32
+// carries at least 2p + 2 significant bits for p = 11 (binary16) and 8
+// (bfloat16), so that equals rounding the exact sum or product.  An activation
+// step reads its table: the library's correctly rounded composition for every
+// input word.
+template <int E>
+__device__ inline uint16_t epi_apply(const EpiArgs& ep, uint16_t t, int m, int n) {
+    for (int s = 0; s < ep.nsteps; ++s) {
+        const int op = ep.ops[s];
+        if (op == kEpiBias) t = narrow<E>(widen<E>(t) + widen<E>(ep.bias[n]));
+        else if (op == kEpiResidual) t = narrow<E>(widen<E>(t) + widen<E>(ep.res[(int64_t)m * ep.ldr + n]));
+        else if (op == kEpiMul) t = narrow<E>(widen<E>(t) * widen<E>(ep.mul[(int64_t)m * ep.ldm + n]));
+        else t = ep.act[(op - kEpiSilu) * kActWords + t];
+    }
+    return t;
+}
+
+// Word-wise on 8 packed words: a binary step (R(W(x) + W(y)) or R(W(x) * W(y)))
+// or a table lookup.
+template <int E, bool MUL>
+__device__ inline u32x4 binop8(u32x4 x, u32x4 y) {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t out = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a = widen<E>((uint16_t)(x[q] >> (16 * h))), b = widen<E>((uint16_t)(y[q] >> (16 * h)));
+            out |= (uint32_t)narrow<E>(MUL ? a * b : a + b) << (16 * h);
+        }
+        r[q] = out;
+    }
+    return r;
+}
+
+__device__ inline u32x4 lookup8(const uint16_t* tab, u32x4 x) {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = (uint32_t)tab[x[q] & 0xffffu] | ((uint32_t)tab[x[q] >> 16] << 16);
+    return r;
+}
+
+// 8 consecutive words src[0..7] of a row, the valid ones only (col + e < N,
+// row valid); 16-byte load when allowed.
+__device__ inline u32x4 load8(const uint16_t* src, bool row_ok, int col, int N, bool vec) {
+    if (row_ok && vec && col + 7 < N) return *(const u32x4*)src;
+    u32x4 r = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (row_ok && col + e < N) r[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+    return r;
+}
+
+__device__ inline void store8(uint16_t* dst, bool row_ok, int col, int N, bool vec, u32x4 v) {
+    if (!row_ok) return;
+    if (vec && col + 7 < N) {
+        *(u32x4*)dst = v;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (col + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+}
+
+// The epilogue inputs of four consecutive outputs (m, nb..nb+3), for kernels that
+// request them before their main loop (only those the program reads; zero for
+// outputs past M or N).
+struct Extras4 {
+    uint16_t b[4], r[4], u[4];
+};
+
+__device__ inline Extras4 epi_prefetch4(const LinearArgs& a, int m, int nb) {
+    const EpiArgs& ep = a.epi;
+    bool ub = false, ur = false, uu = false;
+    for (int s = 0; s < ep.nsteps; ++s) {
+        ub |= ep.ops[s] == kEpiBias;
+        ur |= ep.ops[s] == kEpiResidual;
+        uu |= ep.ops[s] == kEpiMul;
+    }
+    Extras4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool col = nb + e < a.N, ok = col && m < a.M;
+        x.b[e] = (ub && col) ? ep.bias[nb + e] : 0;
+        x.r[e] = (ur && ok) ? ep.res[(int64_t)m * ep.ldr + nb + e] : 0;
+        x.u[e] = (uu && ok) ? ep.mul[(int64_t)m * ep.ldm + nb + e] : 0;
+    }
+    return x;
+}
+
+// The program on four words with their inputs already loaded: the table lookups
+// of an activation step are the only memory accesses, issued together.
+template <int E>
+__device__ inline void epi_apply4(const EpiArgs& ep, uint16_t t[4], const Extras4& x) {
+    for (int s = 0; s < ep.nsteps; ++s) {
+        const int op = ep.ops[s];
+        if (op >= kEpiSilu) {
+            const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = tab[t[e]];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = widen<E>(t[e]);
+                if (op == kEpiBias) t[e] = narrow<E>(v + widen<E>(x.b[e]));
+                else if (op == kEpiResidual) t[e] = narrow<E>(v + widen<E>(x.r[e]));
+                else t[e] = narrow<E>(v * widen<E>(x.u[e]));
+            }
+        }
+    }
+}
+
+// Store four rounded words at (m, nb..nb+3), skipping columns past N.
+__device__ inline void store4_words(const LinearArgs& a, int m, int nb, const uint16_t o[4]) {
+    uint16_t* dst = (uint16_t*)a.y + (int64_t)m * a.ldy + nb;
+    if (a.vec_store && nb + 3 < a.N) {
+        uint2 u;
+        u.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        u.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *(uint2*)dst = u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (nb + e < a.N) dst[e] = o[e];
+    }
+}
+
 // The bias words b[nb..nb+3] widened to FP32 (0 past N), for callers that load
 // them before their main loop so the load latency is off the kernel's tail.
 template <int E>
@@ -166,6 +313,7 @@ __device__ inline void store4(const LinearArgs& a, int m, int nb, float v0, floa
     for (int e = 0; e < 4; ++e) {
         uint16_t p = narrow<E>(v[e]);
         if (MODE == kOutBias) p = narrow<E>(widen<E>(p) + bias[e]);
+        if (MODE == kOutEpi) p = (nb + e < a.N) ? epi_apply<E>(a.epi, p, m, nb + e) : p;
         o[e] = p;
     }
     uint16_t* dst = (uint16_t*)a.y + (int64_t)m * a.ldy + nb;

@@ -189,6 +189,73 @@ __device__ __forceinline__ void order_step() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The epilogue program over a tile of rounded projection words staged in LDS.
+// Layout: row r of the BM x BN tile holds CPR = BN / 8 chunks of 16 bytes, chunk
+// c stored at position c ^ (r % CPR), so that the accumulator-order writes (32
+// rows at one column per instruction) and the row-order reads below both spread
+// over the banks.  Thread tid of NT takes chunks tid, tid + NT, ... (8
+// consecutive columns of one row each) and runs the program step by step over
+// up to 8 of them at a time: each step issues every load it needs before using
+// any, and the extra inputs and y move as 16-byte row accesses where aligned.
+template <int BM, int BN, int NT, int E, int MODE>
+__device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, int m0, int n0, int tid) {
+    constexpr int CPR = BN / 8;
+    constexpr int CHT = BM * CPR / NT;               // chunks per thread
+    constexpr int CH = CHT < 8 ? CHT : 8;            // chunks per pass (bounds register use)
+    static_assert((BM * CPR) % NT == 0 && CHT % CH == 0, "chunks must divide evenly over the threads");
+    const EpiArgs& ep = a.epi;
+    for (int pass = 0; pass < CHT / CH; ++pass) {
+        u32x4 t[CH];
+        int rr[CH], cc[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int c = tid + (pass * CH + k) * NT, r = c / CPR, c8 = c % CPR;
+            t[k] = *(const u32x4*)(tile + (r * CPR + (c8 ^ (r % CPR))) * 16);
+            rr[k] = m0 + r;
+            cc[k] = n0 + c8 * 8;
+        }
+        if constexpr (MODE == kOutBias) {       // the layer's own epilogue: one bias step
+            u32x4 v[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) v[k] = load8(a.b + cc[k], true, cc[k], a.N, ep.vec16 & 2);
+#pragma unroll
+            for (int k = 0; k < CH; ++k) t[k] = binop8<E, false>(t[k], v[k]);
+        }
+        for (int s = 0; MODE == kOutEpi && s < ep.nsteps; ++s) {
+            const int op = ep.ops[s];
+            if (op >= kEpiSilu) {
+                const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
+#pragma unroll
+                for (int k = 0; k < CH; ++k) t[k] = lookup8(tab, t[k]);
+                continue;
+            }
+            u32x4 v[CH];
+            if (op == kEpiBias) {
+#pragma unroll
+                for (int k = 0; k < CH; ++k) v[k] = load8(ep.bias + cc[k], true, cc[k], a.N, ep.vec16 & 2);
+            } else if (op == kEpiResidual) {
+#pragma unroll
+                for (int k = 0; k < CH; ++k)
+                    v[k] = load8(ep.res + (int64_t)rr[k] * ep.ldr + cc[k], rr[k] < a.M, cc[k], a.N, ep.vec16 & 4);
+            } else {
+#pragma unroll
+                for (int k = 0; k < CH; ++k)
+                    v[k] = load8(ep.mul + (int64_t)rr[k] * ep.ldm + cc[k], rr[k] < a.M, cc[k], a.N, ep.vec16 & 8);
+            }
+            if (op == kEpiMul) {
+#pragma unroll
+                for (int k = 0; k < CH; ++k) t[k] = binop8<E, true>(t[k], v[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < CH; ++k) t[k] = binop8<E, false>(t[k], v[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+            store8((uint16_t*)a.y + (int64_t)rr[k] * a.ldy + cc[k], rr[k] < a.M, cc[k], a.N, ep.vec16 & 1, t[k]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Streaming variant for 16-byte aligned layouts (x, weight 16-byte aligned, ldx,
 // ldw and K multiples of 8).
@@ -374,6 +441,32 @@ gemm_stream(LinearArgs a) {
     }
 #undef LIN_ISSUE_ONE
 
+    if constexpr (MODE != kOutF32) {
+        // stage the rounded tile in the (now free) ring, then finish it in row order:
+        // the bias or the epilogue program, and 16-byte stores of whole row chunks
+        static_assert(BM * BN * 2 <= STAGES * SLICE, "the rounded tile must fit in the ring");
+        constexpr int CPR = BN / 8;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int ml = wm * TM + j * 32 + lr;
+                    uint2 u;
+                    u.x = (uint32_t)narrow<E>(acc[i][j][g * 4]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 1]) << 16);
+                    u.y = (uint32_t)narrow<E>(acc[i][j][g * 4 + 2]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 3]) << 16);
+                    const int c8 = nl / 8;
+                    *(uint2*)(smem + (ml * CPR + (c8 ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
+                }
+            }
+        __syncthreads();
+        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x);
+        return;
+    }
+
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -396,6 +489,7 @@ template <int BM, int BN, int WM, int WN, int E>
 static const void* regstaged_fn(int mode) {
     if (mode == kOutBias) return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutBias>;
     if (mode == kOutRound) return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutRound>;
+    if (mode == kOutEpi) return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutEpi>;
     return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutF32>;
 }
 
@@ -403,6 +497,7 @@ template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD>
 static const void* stream_fn(int mode) {
     if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD>;
     if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD>;
+    if (mode == kOutEpi) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutEpi, SPREAD>;
     return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD>;
 }
 

@@ -49,4 +49,10 @@ constexpr int kSkinnyTile = 16;
 constexpr int kSkinnyKStep = 32;
 hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream);
 
+// The activation tables of element type elem on `device` (3 x kActWords words:
+// SiLU, tanh GeLU, erf GeLU), built on `stream` by the first call and waited for
+// there; that first call fails with hipErrorStreamCaptureUnsupported under
+// stream capture.
+hipError_t act_tables(int elem, int device, hipStream_t stream, const uint16_t** tables);
+
 }  // namespace lin

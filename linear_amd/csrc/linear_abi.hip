@@ -48,7 +48,44 @@ struct Request {
     bool need_bias;  // the bias entry point: b must be present
     int elem;        // lin::kF16 or lin::kBF16
     bool f32_out;    // y holds the unrounded FP32 sums
+    const linear_epilogue* epi = nullptr;   // the epilogue entry points: the program
 };
+
+bool epi_uses(const linear_epilogue* ep, int32_t op) {
+    for (int s = 0; s < ep->nsteps; ++s)
+        if (ep->op[s] == op) return true;
+    return false;
+}
+
+// The program's own checks: step count and codes, the extra inputs its steps
+// read, their strides, and overlaps with y (y may be the residual itself, with
+// the same row stride: each element is read before it is written, by the same
+// thread).
+int32_t validate_epilogue(const Request& r) {
+    const linear_epilogue* ep = r.epi;
+    if (!ep) return LINEAR_E_NULL;
+    if (ep->nsteps < 0 || ep->nsteps > LINEAR_EPI_MAX_STEPS) return LINEAR_E_EPILOGUE;
+    for (int s = 0; s < ep->nsteps; ++s)
+        if (ep->op[s] < LINEAR_EPI_BIAS || ep->op[s] > LINEAR_EPI_GELU_ERF) return LINEAR_E_EPILOGUE;
+    if (r.M == 0 || r.N == 0) return LINEAR_OK;
+    const Extent ey = extent(r.y, r.M, r.ldy, r.N);
+    if (epi_uses(ep, LINEAR_EPI_BIAS)) {
+        if (!ep->bias) return LINEAR_E_NULL;
+        if (overlaps(ey, extent(ep->bias, 1, r.N, r.N))) return LINEAR_E_ALIAS;
+    }
+    if (epi_uses(ep, LINEAR_EPI_RESIDUAL)) {
+        if (!ep->residual) return LINEAR_E_NULL;
+        if (ep->ldr < r.N || ep->ldr > kMaxLdOut) return LINEAR_E_STRIDE;
+        const bool in_place = (const void*)ep->residual == r.y && ep->ldr == r.ldy;
+        if (!in_place && overlaps(ey, extent(ep->residual, r.M, ep->ldr, r.N))) return LINEAR_E_ALIAS;
+    }
+    if (epi_uses(ep, LINEAR_EPI_MUL)) {
+        if (!ep->mul) return LINEAR_E_NULL;
+        if (ep->ldm < r.N || ep->ldm > kMaxLdOut) return LINEAR_E_STRIDE;
+        if (overlaps(ey, extent(ep->mul, r.M, ep->ldm, r.N))) return LINEAR_E_ALIAS;
+    }
+    return LINEAR_OK;
+}
 
 // Shape, pointer, stride, alias and path checks.  Pure host logic.
 int32_t validate(const Request& r) {
@@ -67,6 +104,12 @@ int32_t validate(const Request& r) {
     if (overlaps(ey, extent(r.w, r.N, r.ldw, r.K))) return LINEAR_E_ALIAS;
     if (r.b && overlaps(ey, extent(r.b, 1, r.N, r.N))) return LINEAR_E_ALIAS;
     return LINEAR_OK;
+}
+
+int32_t validate_all(const Request& r) {
+    const int32_t st = validate(r);
+    if (st != LINEAR_OK || !r.epi) return st;
+    return validate_epilogue(r);
 }
 
 bool vector_loads_ok(const Request& r) {
@@ -166,7 +209,7 @@ int32_t check_device(int* dev_out) {
 }
 
 int32_t run(const Request& r, void* stream) {
-    int32_t st = validate(r);
+    int32_t st = validate_all(r);
     if (st != LINEAR_OK) return st;
     if (r.M == 0 || r.N == 0) return LINEAR_OK;
     linear_plan p;
@@ -188,7 +231,35 @@ int32_t run(const Request& r, void* stream) {
     a.N = (int)r.N;
     a.K = (int)r.K;
     a.vec_store = vector_store_ok(r) ? 1 : 0;
-    const int mode = r.f32_out ? lin::kOutF32 : (r.b != nullptr ? lin::kOutBias : lin::kOutRound);
+    memset(&a.epi, 0, sizeof a.epi);
+    auto al16 = [](const void* q, int64_t ld) { return ((uintptr_t)q % 16 == 0) && (ld % 8 == 0); };
+    // 16-byte row accesses of the staged epilogue: y and the bias (the program's inputs below)
+    a.epi.vec16 = (al16(r.y, r.ldy) ? 1 : 0) | (al16(r.b, 8) ? 2 : 0);
+    int mode = r.f32_out ? lin::kOutF32 : (r.b != nullptr ? lin::kOutBias : lin::kOutRound);
+    if (r.epi) {
+        mode = lin::kOutEpi;
+        const linear_epilogue* ep = r.epi;
+        a.epi.bias = ep->bias;
+        a.epi.res = ep->residual;
+        a.epi.mul = ep->mul;
+        a.epi.ldr = ep->ldr;
+        a.epi.ldm = ep->ldm;
+        a.epi.nsteps = ep->nsteps;
+        a.epi.vec16 = (al16(r.y, r.ldy) ? 1 : 0) | (al16(ep->bias, 8) ? 2 : 0) |
+                      (al16(ep->residual, ep->ldr) ? 4 : 0) | (al16(ep->mul, ep->ldm) ? 8 : 0);
+        for (int s = 0; s < ep->nsteps; ++s) a.epi.ops[s] = (uint8_t)ep->op[s];
+        if (epi_uses(ep, LINEAR_EPI_SILU) || epi_uses(ep, LINEAR_EPI_GELU_TANH) || epi_uses(ep, LINEAR_EPI_GELU_ERF)) {
+            hipError_t te = lin::act_tables(r.elem, dev, (hipStream_t)stream, &a.epi.act);
+            if (te == hipErrorStreamCaptureUnsupported) {
+                g_last_hip_error = (int32_t)te;
+                return LINEAR_E_CAPTURE;
+            }
+            if (te != hipSuccess) {
+                g_last_hip_error = (int32_t)te;
+                return LINEAR_E_DEVICE;
+            }
+        }
+    }
     const bool vec = p.vector_io != 0;
     hipError_t e;
     if (p.path == LINEAR_PATH_SKINNY) {
@@ -273,6 +344,22 @@ int32_t linear_bf16_f32out(const uint16_t* x, int64_t ldx, const uint16_t* weigh
     return run(r, stream);
 }
 
+int32_t linear_f16_epilogue(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                            const linear_epilogue* epilogue, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                            int64_t K, int32_t path, void* stream) {
+    if (!epilogue) return LINEAR_E_NULL;
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kF16, false, epilogue};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_epilogue(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
+                             const linear_epilogue* epilogue, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t K, int32_t path, void* stream) {
+    if (!epilogue) return LINEAR_E_NULL;
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kBF16, false, epilogue};
+    return run(r, stream);
+}
+
 int32_t linear_f16_plan(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
                         const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         int32_t path, linear_plan* out) {
@@ -294,10 +381,12 @@ const char* linear_status_string(int32_t status) {
         case LINEAR_E_NULL: return "a required pointer is NULL";
         case LINEAR_E_SHAPE: return "invalid shape: M, N or K negative or too large";
         case LINEAR_E_STRIDE: return "invalid row stride: ldx/ldw < K, ldy < N, or beyond the stride limit";
-        case LINEAR_E_ALIAS: return "y overlaps x, weight or b";
+        case LINEAR_E_ALIAS: return "y overlaps x, weight, b or an epilogue input";
         case LINEAR_E_PATH: return "unknown path selector";
         case LINEAR_E_DEVICE: return "no usable gfx950 device is current";
         case LINEAR_E_LAUNCH: return "kernel launch failed";
+        case LINEAR_E_EPILOGUE: return "invalid epilogue program: step count or step code";
+        case LINEAR_E_CAPTURE: return "the first activation epilogue on a device cannot run under stream capture";
         default: return "unknown status";
     }
 }

@@ -62,6 +62,8 @@ skinny_stream(LinearArgs a) {
     const int nb = n0 + (lane >> 4) * 4;
     f32x4 bias = (f32x4){};
     if (MODE == kOutBias && wave == 0) bias = load_bias4<E>(a, nb);
+    Extras4 ex{};
+    if (MODE == kOutEpi && wave == 0) ex = epi_prefetch4(a, m, nb);
     __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc = (f32x4){};
@@ -102,7 +104,13 @@ skinny_stream(LinearArgs a) {
     for (int w = 1; w < WAVES; ++w) s += red[w][lane];
 
     // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
-    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
+    if constexpr (MODE == kOutEpi) {
+        uint16_t o[4] = {narrow<E>(s[0]), narrow<E>(s[1]), narrow<E>(s[2]), narrow<E>(s[3])};
+        epi_apply4<E>(a.epi, o, ex);
+        if (m < a.M) store4_words(a, m, nb, o);
+    } else {
+        if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
+    }
 }
 
 template <int WAVES, int E, int MODE>
@@ -128,6 +136,8 @@ skinny_kernel(LinearArgs a) {
     const int nb = n0 + (lane >> 4) * 4;
     f32x4 bias = (f32x4){};
     if (MODE == kOutBias && wave == 0) bias = load_bias4<E>(a, nb);
+    Extras4 ex{};
+    if (MODE == kOutEpi && wave == 0) ex = epi_prefetch4(a, m, nb);
 
     f32x4 acc = (f32x4){};
     for (int u = ub; u < ue; u += UNROLL) {
@@ -153,7 +163,13 @@ skinny_kernel(LinearArgs a) {
     for (int w = 1; w < WAVES; ++w) s += red[w][lane];
 
     // Accumulator layout: lane l holds column m = l % 16 and rows n = 4 (l / 16) + e.
-    if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
+    if constexpr (MODE == kOutEpi) {
+        uint16_t o[4] = {narrow<E>(s[0]), narrow<E>(s[1]), narrow<E>(s[2]), narrow<E>(s[3])};
+        epi_apply4<E>(a.epi, o, ex);
+        if (m < a.M) store4_words(a, m, nb, o);
+    } else {
+        if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
+    }
 }
 
 template <int E>
@@ -161,10 +177,12 @@ static const void* skinny_fn(bool vec, int mode) {
     if (vec) {
         if (mode == kOutBias) return (const void*)skinny_stream<kSkinnyWaves, E, kOutBias>;
         if (mode == kOutRound) return (const void*)skinny_stream<kSkinnyWaves, E, kOutRound>;
+        if (mode == kOutEpi) return (const void*)skinny_stream<kSkinnyWaves, E, kOutEpi>;
         return (const void*)skinny_stream<kSkinnyWaves, E, kOutF32>;
     }
     if (mode == kOutBias) return (const void*)skinny_kernel<kSkinnyWaves, E, kOutBias>;
     if (mode == kOutRound) return (const void*)skinny_kernel<kSkinnyWaves, E, kOutRound>;
+    if (mode == kOutEpi) return (const void*)skinny_kernel<kSkinnyWaves, E, kOutEpi>;
     return (const void*)skinny_kernel<kSkinnyWaves, E, kOutF32>;
 }
 

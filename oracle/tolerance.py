@@ -43,7 +43,8 @@ BF16 = 1
 def words_to_f64(h, elem: int = F16) -> np.ndarray:
     h = np.asarray(h)
     if elem == BF16:
-        return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if h.dtype == np.float16:
         return h.astype(np.float64)
     return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float64)

@@ -37,8 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_status_strings():
-    for code in range(0, 8):
-        assert la.linear_status_string(code)
+    for code in range(0, 10):
+        assert la.linear_status_string(code) != "unknown status"
     assert la.linear_status_string(99) == "unknown status"
 
 
@@ -106,6 +106,55 @@ def test_k0_allows_null_inputs_until_the_device_check():
 def test_valid_call_without_a_device_reports_device_error():
     assert call() == la.LINEAR_E_DEVICE
     assert la._lib().linear_last_hip_error() != 0
+
+
+R = 0x7F4000000000   # fake residual
+U = 0x7F5000000000   # fake gate input
+
+
+def call_epi(ops, bias=B, res=R, ldr=32, mul=U, ldm=32, y=Y, ldy=32, M=8, N=32, K=64, bf16=False, nsteps=None):
+    ep = la._Epilogue()
+    ep.nsteps = len(ops) if nsteps is None else nsteps
+    for i, o in enumerate(ops[:la.EPI_MAX_STEPS]):
+        ep.op[i] = o
+    ep.bias, ep.residual, ep.ldr, ep.mul, ep.ldm = bias, res, ldr, mul, ldm
+    fn = la._lib().linear_bf16_epilogue if bf16 else la._lib().linear_f16_epilogue
+    return fn(X, 64, W, 64, ctypes.byref(ep), y, ldy, M, N, K, 0, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("bf16", [False, True], ids=["f16", "bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(ops=[], nsteps=-1), la.LINEAR_E_EPILOGUE),
+    (dict(ops=[1] * 9, nsteps=9), la.LINEAR_E_EPILOGUE),
+    (dict(ops=[7]), la.LINEAR_E_EPILOGUE),
+    (dict(ops=[0]), la.LINEAR_E_EPILOGUE),
+    (dict(ops=[la.EPI_BIAS], bias=0), la.LINEAR_E_NULL),
+    (dict(ops=[la.EPI_RESIDUAL], res=0), la.LINEAR_E_NULL),
+    (dict(ops=[la.EPI_MUL], mul=0), la.LINEAR_E_NULL),
+    (dict(ops=[la.EPI_RESIDUAL], ldr=31), la.LINEAR_E_STRIDE),
+    (dict(ops=[la.EPI_MUL], ldm=31), la.LINEAR_E_STRIDE),
+    (dict(ops=[la.EPI_RESIDUAL], res=Y + 64), la.LINEAR_E_ALIAS),              # residual offset inside y
+    (dict(ops=[la.EPI_RESIDUAL], res=Y, ldr=40), la.LINEAR_E_ALIAS),           # same start, other stride
+    (dict(ops=[la.EPI_MUL], mul=Y), la.LINEAR_E_ALIAS),                        # y may not be the gate input
+    (dict(ops=[la.EPI_BIAS], bias=Y + 6), la.LINEAR_E_ALIAS),
+    (dict(ops=[la.EPI_BIAS, la.EPI_SILU], y=0), la.LINEAR_E_NULL),
+])
+def test_epilogue_validation(kw, code, bf16):
+    assert call_epi(bf16=bf16, **kw) == code
+
+
+@needs_lib
+def test_epilogue_unused_inputs_may_be_null_and_in_place_residual_is_accepted():
+    # the inputs a program does not read are never checked; the residual may be y itself
+    no_dev = not torch.cuda.is_available()
+    for kw in (dict(ops=[la.EPI_SILU], bias=0, res=0, mul=0), dict(ops=[], bias=0, res=0, mul=0),
+               dict(ops=[la.EPI_BIAS, la.EPI_RESIDUAL], res=Y, ldr=32, mul=0)):
+        rc = call_epi(**kw)
+        assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
+        if no_dev:
+            assert rc == la.LINEAR_E_DEVICE
+    assert la._lib().linear_f16_epilogue(X, 64, W, 64, None, Y, 32, 8, 32, 64, 0, None) == la.LINEAR_E_NULL
 
 
 def plan(M, N, K, path=0, x=X, w=W, ldx=None, ldw=None):

@@ -441,6 +441,56 @@ gemm_stream(LinearArgs a) {
     }
 #undef LIN_ISSUE_ONE
 
+    if constexpr (MODE == kOutF32) {
+        // the FP32 sums go out the same way, staged as floats in the freed ring
+        // (in row bands when the whole tile does not fit): row r of a band holds
+        // BN / 4 chunks of 16 bytes, chunk c at position c ^ (r % (BN / 4))
+        constexpr int CPR4 = BN / 4;
+        constexpr int PASSES = (BM * BN * 4 + STAGES * SLICE - 1) / (STAGES * SLICE);
+        constexpr int RPP = BM / PASSES;                   // rows per band
+        static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
+        constexpr int NT = NW * 64;
+        constexpr int CHT = RPP * CPR4 / NT;
+        static_assert((RPP * CPR4) % NT == 0, "chunks must divide evenly over the threads");
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
+                        if (ml >= 0 && ml < RPP) {
+                            const f32x4 v = (f32x4){acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                                    acc[i][j][g * 4 + 3]};
+                            *(f32x4*)(smem + (ml * CPR4 + ((nl / 4) ^ (ml % CPR4))) * 16) = v;
+                        }
+                    }
+                }
+            __syncthreads();
+            const bool vec = a.vec_store && ((uintptr_t)a.y % 16 == 0);
+#pragma unroll
+            for (int k = 0; k < CHT; ++k) {
+                const int c = (int)threadIdx.x + k * NT, r = c / CPR4, c4 = c % CPR4;
+                const f32x4 v = *(const f32x4*)(smem + (r * CPR4 + (c4 ^ (r % CPR4))) * 16);
+                const int m = m0 + pass * RPP + r, n = n0 + c4 * 4;
+                if (m >= a.M) continue;
+                float* dst = (float*)a.y + (int64_t)m * a.ldy + n;
+                if (vec && n + 3 < a.N) {
+                    *(f32x4*)dst = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) dst[e] = v[e];
+                }
+            }
+        }
+        return;
+    }
+
     if constexpr (MODE != kOutF32) {
         // stage the rounded tile in the (now free) ring, then finish it in row order:
         // the bias or the epilogue program, and 16-byte stores of whole row chunks

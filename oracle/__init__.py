@@ -82,6 +82,15 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_epilogue.restype = None
     lib.oracle_unary_array.argtypes = [ctypes.c_int, ctypes.c_int, _u16p, _u16p, _i64]
     lib.oracle_unary_array.restype = None
+    lib.oracle_grouped.argtypes = [ctypes.c_int, _u16p, _i64, _i64, _u16p, _i64, _u16p, _u16p, _u16p, _f32p, _i64,
+                                   _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_grouped.restype = ctypes.c_int
+    lib.oracle_indexed.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _i64, _i32p, _u16p, _f32p, _i64,
+                                   _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_indexed.restype = None
+    lib.oracle_indexed_band.argtypes = [ctypes.c_int, _u16p, _i64, _u16p, _i64, _i64, _i32p, _f64p, _f64p,
+                                        _i64, _i64, _i64, _i64]
+    lib.oracle_indexed_band.restype = None
     lib.oracle_bf16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
     lib.oracle_bf16_to_f32_array.restype = None
     lib.oracle_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
@@ -247,6 +256,58 @@ class Oracle:
                                   _ptr(A, ctypes.c_double), nthreads)
         if rc != 0:
             raise MemoryError("oracle_band_f64 failed")
+        return S, A
+
+    # -- grouped and indexed contractions ------------------------------------------
+    def grouped(self, x, w, b=None, elem: int = F16, nthreads: int = 0):
+        """x: [G, M, K] words, w: [G*N, K], b: [G*N] or None.  Returns (y, proj, y32) as
+        [G, M, N] arrays (y = proj when b is None)."""
+        x = _as_words(x)
+        w = _as_words(w)
+        G, M, K = x.shape
+        N = w.shape[0] // max(G, 1)
+        assert w.shape == (G * N, K), (x.shape, w.shape)
+        bb = None if b is None else _as_words(b)
+        y = np.zeros((G, M, N), np.uint16)
+        proj = np.zeros((G, M, N), np.uint16)
+        y32 = np.zeros((G, M, N), np.float32)
+        rc = self.lib.oracle_grouped(int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), M * max(K, 1),
+                                     _ptr(w, ctypes.c_uint16), max(K, 1),
+                                     None if bb is None else _ptr(bb, ctypes.c_uint16), _ptr(y, ctypes.c_uint16),
+                                     _ptr(proj, ctypes.c_uint16), _ptr(y32, ctypes.c_float), max(N, 1), M * max(N, 1),
+                                     G, M, N, K, nthreads)
+        if rc != 0:
+            raise MemoryError("oracle_grouped failed")
+        return y, proj, y32
+
+    def indexed(self, x, w, idx, elem: int = F16, y_init=None, nthreads: int = 0):
+        """x: [M, K] words, w: [E, K, N] words, idx: [M] int32.  Returns (y, y32) [M, N];
+        rows whose idx is outside [0, E) keep y_init (zeros by default)."""
+        x = _as_words(x)
+        w = _as_words(w)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        M, K = x.shape
+        E, K2, N = w.shape
+        assert K == K2 and idx.shape == (M,)
+        y = np.zeros((M, N), np.uint16) if y_init is None else np.array(y_init, np.uint16, copy=True)
+        y32 = np.zeros((M, N), np.float32)
+        self.lib.oracle_indexed(int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16),
+                                max(N, 1), max(K, 1) * max(N, 1), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                _ptr(y, ctypes.c_uint16), _ptr(y32, ctypes.c_float), max(N, 1), E, M, N, K, nthreads)
+        return y, y32
+
+    def indexed_band(self, x, w, idx, elem: int = F16):
+        x = _as_words(x)
+        w = _as_words(w)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        M, K = x.shape
+        E, _, N = w.shape
+        S = np.zeros((M, N), np.float64)
+        A = np.zeros((M, N), np.float64)
+        self.lib.oracle_indexed_band(int(elem), _ptr(x, ctypes.c_uint16), max(K, 1), _ptr(w, ctypes.c_uint16),
+                                     max(N, 1), max(K, 1) * max(N, 1),
+                                     idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     _ptr(S, ctypes.c_double), _ptr(A, ctypes.c_double), E, M, N, K)
         return S, A
 
     # -- multi-step epilogue ------------------------------------------------------

@@ -495,3 +495,85 @@ void oracle_unary_array(int elem, int op, const uint16_t* x, uint16_t* out, int6
         else out[i] = epi_step(elem, op, x[i], 0, 0, 0);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Grouped and indexed contractions ("The Graph IR", op table).
+ *
+ * GroupedDenseContraction: a [G*N, K] weight read as G blocks of N rows against
+ * a [G, M, K] activation, giving [G, M, N]: group g contracts activation slice
+ * g with weight rows g*N .. g*N+N-1, each block read in place.
+ *
+ * IndexedMatMul: x [M, K], W [E, K, N], idx [M] -> [M, N]: row m contracts
+ * against expert idx[m], y[m, n] = sum_k x[m, k] * W[idx[m], k, n]; the expert
+ * tables are read in place (note the [K, N] order of each expert: the weight
+ * is indexed by k first).
+ *
+ * Readings: operands are element-type words (binary16 or bfloat16) as for the
+ * layer; accumulation is FP32 in sequential k from +0; the result is rounded to
+ * the element type, or returned as the FP32 sums; a grouped call may add a
+ * [G*N] bias as the layer does.  A row whose idx lies outside [0, E) has no
+ * expert: the oracle leaves its outputs untouched (the kernels do the same).
+ * ------------------------------------------------------------------------- */
+
+/* x: [G, M, K] with row stride ldx and group stride sx; w: [G*N, K] row stride
+   ldw; b: [G*N] or NULL; y/proj: [G, M, N] row stride ldy, group stride sy;
+   y32: FP32 sums, same layout (each may be NULL). */
+int oracle_grouped(int elem, const uint16_t* x, int64_t ldx, int64_t sx, const uint16_t* w, int64_t ldw,
+                   const uint16_t* b, uint16_t* y, uint16_t* proj, float* y32, int64_t ldy, int64_t sy,
+                   int64_t G, int64_t M, int64_t N, int64_t K, int nthreads) {
+    for (int64_t g = 0; g < G; ++g) {
+        int rc = oracle_linear(elem, x + g * sx, ldx, w + g * N * ldw, ldw, b ? b + g * N : NULL,
+                               y ? y + g * sy : NULL, proj ? proj + g * sy : NULL, y32 ? y32 + g * sy : NULL,
+                               ldy, M, N, K, nthreads);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}
+
+/* x: [M, K] row stride ldx; w: [E, K, N] with row stride ldw (>= N, between k
+   rows) and expert stride sw (>= K*ldw); idx: [M]; y: [M, N] row stride ldy
+   (rounded), y32: FP32 sums (each may be NULL). */
+void oracle_indexed(int elem, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                    const int32_t* idx, uint16_t* y, float* y32, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                    int64_t K, int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const int64_t e = idx[m];
+        if (e < 0 || e >= E) continue;
+        const uint16_t* we = w + e * sw;
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) acc = acc + widen16(elem, x[m * ldx + k]) * widen16(elem, we[k * ldw + n]);
+            if (y32) y32[m * ldy + n] = acc;
+            if (y) y[m * ldy + n] = narrow16(elem, acc);
+        }
+    }
+}
+
+/* FP64 band data S = sum x*w and A = sum |x*w| of the indexed contraction
+   (rows without an expert get 0). */
+void oracle_indexed_band(int elem, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                         const int32_t* idx, double* S, double* A, int64_t E, int64_t M, int64_t N, int64_t K) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const int64_t e = idx[m];
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, a = 0.0;
+            if (e >= 0 && e < E) {
+                const uint16_t* we = w + e * sw;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double pd = (double)widen16(elem, x[m * ldx + k]) * (double)widen16(elem, we[k * ldw + n]);
+                    s += pd;
+                    a += fabs(pd);
+                }
+            }
+            S[m * N + n] = s;
+            A[m * N + n] = a;
+        }
+    }
+}

@@ -7,6 +7,7 @@ import pytest
 import oracle
 import pins
 import pins_epilogue
+import pins_grouped
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -100,6 +101,41 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
             caught.append(pin.__name__)
             break
     assert caught, "no pin catches mutant " + name
+
+
+# Mistakes in the grouped and indexed contractions, caught by their pins.
+GROUPED_MUTANTS = [
+    ("grouped_weight_block_stride", "int rc = oracle_linear(elem, x + g * sx, ldx, w + g * N * ldw, ldw,",
+     "int rc = oracle_linear(elem, x + g * sx, ldx, w + g * ldw, ldw,"),
+    ("grouped_bias_not_offset", "b ? b + g * N : NULL,", "b,"),
+    ("grouped_activation_stride", "int rc = oracle_linear(elem, x + g * sx, ldx,", "int rc = oracle_linear(elem, x, ldx,"),
+    ("indexed_next_expert", "const uint16_t* we = w + e * sw;\n        for (int64_t n = 0; n < N; ++n) {\n            float acc",
+     "const uint16_t* we = w + ((e + 1) % E) * sw;\n        for (int64_t n = 0; n < N; ++n) {\n            float acc"),
+    ("indexed_reversed_columns", "widen16(elem, we[k * ldw + n]);", "widen16(elem, we[k * ldw + (N - 1 - n)]);"),
+    ("indexed_writes_rows_without_expert", "        if (e < 0 || e >= E) continue;\n        const uint16_t* we = w + e * sw;\n        for (int64_t n = 0; n < N; ++n) {\n            float acc",
+     "        if (e < 0 || e >= E) { for (int64_t n = 0; n < N; ++n) if (y) y[m * ldy + n] = 0; continue; }\n        const uint16_t* we = w + e * sw;\n        for (int64_t n = 0; n < N; ++n) {\n            float acc"),
+    ("indexed_drops_first_k", "for (int64_t k = 0; k < K; ++k) acc = acc + widen16(elem, x[m * ldx + k])",
+     "for (int64_t k = 1; k < K; ++k) acc = acc + widen16(elem, x[m * ldx + k])"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GROUPED_MUTANTS, ids=[m[0] for m in GROUPED_MUTANTS])
+def test_grouped_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site vanished: " + name
+    mutated = src.replace(old, new, 1)
+    path = str(tmp_path / ("m_%s.c" % name))
+    open(path, "w").write(mutated)
+    lib = oracle.build(src=path, out=str(tmp_path / ("lib_%s.so" % name)))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in pins_grouped.GROUPED_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, "no grouped pin catches mutant " + name
 
 
 @pytest.mark.parametrize("name,old,new", EPI_MUTANTS, ids=[m[0] for m in EPI_MUTANTS])

@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
     ap.add_argument("--variant", default="f16", help="with --only: f16, bf16, f16_f32out, bf16_f32out or "
-                    "<f16|bf16>_epi_<gelu|res|silu_mul|silu>")
+                    "<f16|bf16>_epi_<gelu|res|silu_mul|silu>; f16 or bf16 for grouped, moe_decode, moe_prefill")
     ap.add_argument("--no-variants", action="store_true", help="skip the bfloat16 / FP32-output timings")
     ap.add_argument("--record-traffic", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR"),
@@ -286,6 +286,61 @@ def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
     }
 
 
+def bench_grouped(name, torch, la, workloads, stream, calls, dtype_name="f16"):
+    """The grouped contraction workload (G groups), in TFLOP/s."""
+    wl = workloads.GROUPED[name]
+    dtype = torch.bfloat16 if dtype_name == "bf16" else torch.float16
+    fn = la.linear_bf16_grouped if dtype == torch.bfloat16 else la.linear_f16_grouped
+    x, w, b = workloads.make_grouped_inputs(wl.G, wl.M, wl.N, wl.K, wl.a, seed=0, device="cuda", dtype=dtype)
+    sets = rotation_sets(wl.bytes)
+    xs = [x] + [x.clone() for _ in range(sets - 1)]
+    ws = [w] + [w.clone() for _ in range(sets - 1)]
+    ys = [torch.empty((wl.G, wl.M, wl.N), dtype=dtype, device="cuda") for _ in range(sets)]
+
+    def call(i):
+        k = i % sets
+        fn(xs[k], ws[k], b, out=ys[k], stream=stream)
+
+    graph = capture(call, sets, stream, torch)
+    replays = max(1, calls // sets)
+    graph.replay()
+    times = [time_region(graph, replays, stream, torch) for _ in range(5)]
+    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    del graph, xs, ws, ys
+    return {"G": wl.G, "M": wl.M, "N": wl.N, "K": wl.K, "variant": dtype_name,
+            "us_per_call": round(ms * 1e3, 3), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 1),
+            "frac_mfma_peak": round(wl.flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4), "input_sets": sets}
+
+
+def bench_indexed(name, torch, la, workloads, stream, calls, dtype_name="f16"):
+    """The indexed (expert) contraction: TFLOP/s, and HBM GB/s over the algorithmic
+    bytes (x, the tables of the experts idx selects, idx, y)."""
+    wl = workloads.INDEXED[name]
+    dtype = torch.bfloat16 if dtype_name == "bf16" else torch.float16
+    fn = la.linear_bf16_indexed if dtype == torch.bfloat16 else la.linear_f16_indexed
+    x, w, idx = workloads.make_indexed_inputs(wl.E, wl.M, wl.N, wl.K, wl.a, seed=0, device="cuda", dtype=dtype)
+    used = int(torch.unique(idx).numel())
+    nbytes = 2 * wl.M * wl.K + 2 * used * wl.K * wl.N + 4 * wl.M + 2 * wl.M * wl.N
+    sets = rotation_sets(nbytes)
+    ws = [w] + [w.clone() for _ in range(sets - 1)]
+    ys = [torch.empty((wl.M, wl.N), dtype=dtype, device="cuda") for _ in range(sets)]
+
+    def call(i):
+        k = i % sets
+        fn(x, ws[k], idx, out=ys[k], stream=stream)
+
+    graph = capture(call, sets, stream, torch)
+    replays = max(1, calls // sets)
+    graph.replay()
+    times = [time_region(graph, replays, stream, torch) for _ in range(5)]
+    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    del graph, ws, ys
+    return {"E": wl.E, "M": wl.M, "N": wl.N, "K": wl.K, "experts_used": used, "variant": dtype_name,
+            "us_per_call": round(ms * 1e3, 3), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 1),
+            "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "input_sets": sets}
+
+
 def cpu_baseline(workloads, target_s: float = 10.0):
     """The CPU oracle on the same decode step, repeated until ~target_s of CPU work."""
     import oracle
@@ -356,6 +411,10 @@ def main():
             dt = torch.bfloat16 if args.variant == "bf16" else torch.float16
             ms, _ = bench_decode(args, torch, la, workloads, stream, dt)
             log("decode ms/step %.5f" % ms)
+        elif args.only in workloads.GROUPED:
+            log(json.dumps(bench_grouped(args.only, torch, la, workloads, stream, 40, args.variant)))
+        elif args.only in workloads.INDEXED:
+            log(json.dumps(bench_indexed(args.only, torch, la, workloads, stream, 200, args.variant)))
         else:
             log(json.dumps(bench_gemm(args.only, torch, la, workloads, stream, 100, args.variant)))
         return
@@ -390,6 +449,11 @@ def main():
                                      ("mlp_up", 30, "f16_epi_gelu"), ("down", 50, "f16_epi_res"),
                                      ("attn", 50, "f16_epi_silu_mul"), ("gemv16", 400, "f16_epi_silu")):
                 variants["%s_%s" % (name, var)] = r = bench_gemm(name, torch, la, workloads, stream, calls, var)
+                log(json.dumps(r))
+            variants["grouped_f16"] = r = bench_grouped("grouped", torch, la, workloads, stream, 40)
+            log(json.dumps(r))
+            for name, calls in (("moe_decode", 400), ("moe_prefill", 40)):
+                variants["%s_f16" % name] = r = bench_indexed(name, torch, la, workloads, stream, calls)
                 log(json.dumps(r))
     torch.cuda.synchronize()
 

@@ -218,6 +218,87 @@ int32_t linear_bf16_epilogue(const uint16_t* x, int64_t ldx,
                              int64_t M, int64_t N, int64_t K,
                              int32_t path, void* stream);
 
+/*
+ * Grouped contraction ("The Graph IR", op table: GroupedDenseContraction): a
+ * [G*N, K] weight read in place as G blocks of N rows against a [G, M, K]
+ * activation, giving [G, M, N]:
+ *
+ *     y[g, m, n] = RNE_E( sum_k x[g, m, k] * weight[g*N + n, k] )   (+ b[g*N + n] as in linear_*)
+ *
+ * x: group g at x + g * sx, rows with stride ldx (sx in elements, >= 0; slices may
+ * overlap, they are only read); weight: [G*N, K] with row stride ldw; b: [G*N] or
+ * NULL (NULL: the projection alone); y: group g at y + g * sy, row stride ldy,
+ * sy >= (M-1)*ldy + N so that groups write disjoint outputs.  Element type,
+ * rounding, bias epilogue, paths, reruns and errors as for linear_f16_ex (G up to
+ * 65535); each group is exactly linear_f16_ex on its slices.  The _f32out forms
+ * return the unrounded FP32 sums (the op table gives this contraction an f32
+ * output).  The op table's f32 activation is read here in the weight's element
+ * type: the MFMA path multiplies 16-bit operands.
+ */
+int32_t linear_f16_grouped(const uint16_t* x, int64_t ldx, int64_t sx,
+                           const uint16_t* weight, int64_t ldw,
+                           const uint16_t* b,
+                           uint16_t* y, int64_t ldy, int64_t sy,
+                           int64_t G, int64_t M, int64_t N, int64_t K,
+                           int32_t path, void* stream);
+int32_t linear_bf16_grouped(const uint16_t* x, int64_t ldx, int64_t sx,
+                            const uint16_t* weight, int64_t ldw,
+                            const uint16_t* b,
+                            uint16_t* y, int64_t ldy, int64_t sy,
+                            int64_t G, int64_t M, int64_t N, int64_t K,
+                            int32_t path, void* stream);
+int32_t linear_f16_grouped_f32out(const uint16_t* x, int64_t ldx, int64_t sx,
+                                  const uint16_t* weight, int64_t ldw,
+                                  float* y, int64_t ldy, int64_t sy,
+                                  int64_t G, int64_t M, int64_t N, int64_t K,
+                                  int32_t path, void* stream);
+int32_t linear_bf16_grouped_f32out(const uint16_t* x, int64_t ldx, int64_t sx,
+                                   const uint16_t* weight, int64_t ldw,
+                                   float* y, int64_t ldy, int64_t sy,
+                                   int64_t G, int64_t M, int64_t N, int64_t K,
+                                   int32_t path, void* stream);
+
+/*
+ * Indexed contraction ("The Graph IR", op table: IndexedMatMul; "Tracing a
+ * Model", section "Mixture-of-experts routing": each row contracts against its
+ * own expert, the expert tables read in place):
+ *
+ *     y[m, n] = RNE_E( sum_k x[m, k] * w[idx[m], k, n] )      (FP32 accumulation)
+ *
+ * x: [M, K], row stride ldx >= K.  w: E expert tables of [K, N] (k first, n
+ * contiguous): element (e, k, n) at w[e * sw + k * ldw + n], ldw >= N,
+ * sw >= K * ldw.  idx: [M] device int32.  y: [M, N], row stride ldy >= N.  A row
+ * whose idx lies outside [0, E) has no expert and its outputs are left untouched.
+ * Only rows m < M and columns n < N are written; reruns are bit-identical.
+ * E up to 65535; M, N, K < 2^31.  The _f32out forms store the unrounded sums.
+ * Errors as for linear_f16_ex (y overlapping x, w or idx is LINEAR_E_ALIAS);
+ * E == 0, M == 0 or N == 0 is a successful no-op.
+ */
+int32_t linear_f16_indexed(const uint16_t* x, int64_t ldx,
+                           const uint16_t* w, int64_t ldw, int64_t sw,
+                           const int32_t* idx,
+                           uint16_t* y, int64_t ldy,
+                           int64_t E, int64_t M, int64_t N, int64_t K,
+                           void* stream);
+int32_t linear_bf16_indexed(const uint16_t* x, int64_t ldx,
+                            const uint16_t* w, int64_t ldw, int64_t sw,
+                            const int32_t* idx,
+                            uint16_t* y, int64_t ldy,
+                            int64_t E, int64_t M, int64_t N, int64_t K,
+                            void* stream);
+int32_t linear_f16_indexed_f32out(const uint16_t* x, int64_t ldx,
+                                  const uint16_t* w, int64_t ldw, int64_t sw,
+                                  const int32_t* idx,
+                                  float* y, int64_t ldy,
+                                  int64_t E, int64_t M, int64_t N, int64_t K,
+                                  void* stream);
+int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx,
+                                   const uint16_t* w, int64_t ldw, int64_t sw,
+                                   const int32_t* idx,
+                                   float* y, int64_t ldy,
+                                   int64_t E, int64_t M, int64_t N, int64_t K,
+                                   void* stream);
+
 /* Which kernel a call would launch.  Pure host function: touches no device. */
 typedef struct linear_plan {
     int32_t path;       /* LINEAR_PATH_GEMM or LINEAR_PATH_SKINNY */

@@ -43,6 +43,8 @@ PATH_SKINNY = 2
 ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_f32out",
                 "linear_bf16", "linear_bf16_nobias", "linear_bf16_ex", "linear_bf16_f32out",
                 "linear_f16_epilogue", "linear_bf16_epilogue",
+                "linear_f16_grouped", "linear_bf16_grouped", "linear_f16_grouped_f32out", "linear_bf16_grouped_f32out",
+                "linear_f16_indexed", "linear_bf16_indexed", "linear_f16_indexed_f32out", "linear_bf16_indexed_f32out",
                 "linear_f16_plan", "linear_status_string", "linear_last_hip_error")
 
 
@@ -102,6 +104,16 @@ def _lib():
         getattr(lib, name).restype = i32
     for name in ("linear_f16_epilogue", "linear_bf16_epilogue"):
         getattr(lib, name).argtypes = [vp, i64, vp, i64, ctypes.POINTER(_Epilogue), vp, i64, i64, i64, i64, i32, vp]
+        getattr(lib, name).restype = i32
+    for name in ("linear_f16_grouped", "linear_bf16_grouped"):
+        getattr(lib, name).argtypes = [vp, i64, i64, vp, i64, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
+        getattr(lib, name).restype = i32
+    for name in ("linear_f16_grouped_f32out", "linear_bf16_grouped_f32out"):
+        getattr(lib, name).argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, i64, i64, i64, i64, i32, vp]
+        getattr(lib, name).restype = i32
+    for name in ("linear_f16_indexed", "linear_bf16_indexed", "linear_f16_indexed_f32out",
+                 "linear_bf16_indexed_f32out"):
+        getattr(lib, name).argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64, vp]
         getattr(lib, name).restype = i32
     lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
                                     ctypes.POINTER(_Plan)]
@@ -288,6 +300,114 @@ def linear_bf16_epilogue(x: torch.Tensor, weight: torch.Tensor, ops, bias=None, 
     """linear_f16_epilogue on bfloat16 operands, inputs and output."""
     return _epilogue_call("linear_bf16_epilogue", torch.bfloat16, x, weight, ops, bias, residual, mul, out, path,
                           stream)
+
+
+def _grouped_call(dtype, x, weight, b, out, f32, path, stream):
+    """x [G, M, K] (inner two dims row-major), weight [G*N, K], b [G*N] or None."""
+    if x.dtype != dtype or weight.dtype != dtype:
+        raise TypeError("x and weight must be %s" % dtype)
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [G, M, K] and weight [G*N, K]")
+    G, M, K = x.shape
+    if G == 0 or weight.shape[0] % max(G, 1) != 0 or weight.shape[1] != K:
+        raise ValueError("weight must be [G*N, %d] for G = %d" % (K, G))
+    N = weight.shape[0] // G
+    if (K > 1 and x.stride(2) != 1) or (K > 1 and weight.stride(1) != 1):
+        raise ValueError("x and weight need unit inner stride")
+    ldx = x.stride(1) if M > 1 else max(K, x.stride(1), 1)
+    sx = x.stride(0)
+    ldw = weight.stride(0) if weight.shape[0] > 1 else max(K, 1)
+    out_dtype = torch.float32 if f32 else dtype
+    if out is None:
+        out = torch.empty((G, M, N), dtype=out_dtype, device=x.device)
+    if out.dtype != out_dtype or tuple(out.shape) != (G, M, N) or (N > 1 and out.stride(2) != 1):
+        raise ValueError("out must be a %s [%d, %d, %d] tensor with unit inner stride" % (out_dtype, G, M, N))
+    ldy = out.stride(1) if M > 1 else max(N, out.stride(1), 1)
+    sy = out.stride(0)
+    bp = None
+    if b is not None:
+        if f32:
+            raise ValueError("the FP32-output grouped call takes no bias")
+        if b.dtype != dtype or b.dim() != 1 or b.shape[0] != G * N or (G * N > 1 and b.stride(0) != 1):
+            raise ValueError("b must be a contiguous %s [G*N] tensor" % dtype)
+        bp = b.data_ptr()
+    tag = "bf16" if dtype == torch.bfloat16 else "f16"
+    if f32:
+        name = "linear_%s_grouped_f32out" % tag
+        rc = getattr(_lib(), name)(x.data_ptr(), ldx, sx, weight.data_ptr(), ldw, out.data_ptr(), ldy, sy, G, M, N,
+                                   K, int(path), _stream_handle(stream, x, out))
+    else:
+        name = "linear_%s_grouped" % tag
+        rc = getattr(_lib(), name)(x.data_ptr(), ldx, sx, weight.data_ptr(), ldw, bp, out.data_ptr(), ldy, sy, G, M,
+                                   N, K, int(path), _stream_handle(stream, x, out))
+    _check(rc, name)
+    return out
+
+
+def linear_f16_grouped(x, weight, b=None, out=None, path: int = PATH_AUTO, stream=None):
+    """Grouped contraction: x [G, M, K] against weight [G*N, K] read as G blocks of N rows."""
+    return _grouped_call(torch.float16, x, weight, b, out, False, path, stream)
+
+
+def linear_bf16_grouped(x, weight, b=None, out=None, path: int = PATH_AUTO, stream=None):
+    return _grouped_call(torch.bfloat16, x, weight, b, out, False, path, stream)
+
+
+def linear_f16_grouped_f32out(x, weight, out=None, path: int = PATH_AUTO, stream=None):
+    return _grouped_call(torch.float16, x, weight, None, out, True, path, stream)
+
+
+def linear_bf16_grouped_f32out(x, weight, out=None, path: int = PATH_AUTO, stream=None):
+    return _grouped_call(torch.bfloat16, x, weight, None, out, True, path, stream)
+
+
+def _indexed_call(dtype, x, w, idx, out, f32, stream):
+    """x [M, K], w [E, K, N] (inner two dims row-major), idx [M] int32."""
+    if x.dtype != dtype or w.dtype != dtype:
+        raise TypeError("x and w must be %s" % dtype)
+    if idx.dtype != torch.int32 or idx.dim() != 1 or (idx.shape[0] > 1 and idx.stride(0) != 1):
+        raise TypeError("idx must be a contiguous int32 [M] tensor")
+    xp, ldx = _mat(x, "x", dtype)
+    if w.dim() != 3:
+        raise ValueError("w must be [E, K, N]")
+    E, K, N = w.shape
+    M = x.shape[0]
+    if x.shape[1] != K or idx.shape[0] != M:
+        raise ValueError("x is %s, w is %s, idx is %s" % (tuple(x.shape), tuple(w.shape), tuple(idx.shape)))
+    if N > 1 and w.stride(2) != 1:
+        raise ValueError("w needs unit inner stride")
+    ldw = w.stride(1) if K > 1 else max(N, w.stride(1), 1)
+    sw = w.stride(0) if E > 1 else max(K * ldw, w.stride(0), 1)
+    out_dtype = torch.float32 if f32 else dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    yp, ldy = _mat(out, "out", out_dtype)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [%d, %d]" % (M, N))
+    tag = "bf16" if dtype == torch.bfloat16 else "f16"
+    name = "linear_%s_indexed%s" % (tag, "_f32out" if f32 else "")
+    rc = getattr(_lib(), name)(xp, ldx, w.data_ptr(), ldw, sw, idx.data_ptr(), yp, ldy, E, M, N, K,
+                               _stream_handle(stream, x, out))
+    _check(rc, name)
+    return out
+
+
+def linear_f16_indexed(x, w, idx, out=None, stream=None):
+    """Indexed contraction: row m of x against expert table w[idx[m]] ([K, N]); rows whose
+    idx has no expert keep out's contents."""
+    return _indexed_call(torch.float16, x, w, idx, out, False, stream)
+
+
+def linear_bf16_indexed(x, w, idx, out=None, stream=None):
+    return _indexed_call(torch.bfloat16, x, w, idx, out, False, stream)
+
+
+def linear_f16_indexed_f32out(x, w, idx, out=None, stream=None):
+    return _indexed_call(torch.float16, x, w, idx, out, True, stream)
+
+
+def linear_bf16_indexed_f32out(x, w, idx, out=None, stream=None):
+    return _indexed_call(torch.bfloat16, x, w, idx, out, True, stream)
 
 
 def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,

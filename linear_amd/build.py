@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblinear_amd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "skinny.hip", "epilogue.hip", "linear_abi.hip"]
+SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "skinny.hip", "epilogue.hip", "indexed.hip", "linear_abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -45,7 +45,10 @@ struct LinearArgs {
     int tiles_m, tiles_n;
     int vec_store;       // 1: y aligned for 4-element vector stores and ldy % 4 == 0
     EpiArgs epi;         // the epilogue program (kOutEpi only)
+    int64_t gsx, gsy;    // grouped calls (gridDim.z groups): x and y group strides in elements
+    int groups;          // gridDim.z (1 for ungrouped calls)
 };
+
 
 // Element types of x, weight, b and (rounded) y.
 enum : int { kF16 = 0, kBF16 = 1 };
@@ -54,6 +57,19 @@ enum : int { kF16 = 0, kBF16 = 1 };
 // round again); round only; store the FP32 sum itself; or round and run the
 // epilogue program of a.epi.
 enum : int { kOutBias = 0, kOutRound = 1, kOutF32 = 2, kOutEpi = 3 };
+
+// Grouped contraction: workgroup z handles group z, the activation slice
+// x + z * gsx, the weight block of rows z * N .. z * N + N - 1, y + z * gsy and the
+// bias words z * N ...  (no-op for ungrouped launches, gridDim.z == 1).
+template <int MODE>
+__device__ inline void enter_group(LinearArgs& a) {
+    const int64_t g = blockIdx.z;
+    if (g == 0) return;
+    a.x += g * a.gsx;
+    a.w += g * (int64_t)a.N * a.ldw;
+    a.y = (void*)((char*)a.y + g * a.gsy * (MODE == kOutF32 ? 4 : 2));
+    if (a.b) a.b += g * (int64_t)a.N;
+}
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, no stride.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;

@@ -61,6 +61,7 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, i
 template <int BM, int BN, int WM, int WN, int E, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(LinearArgs a) {
+    enter_group<MODE>(a);
     constexpr int BK = 64;
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;   // one wave's output tile (m x n)
@@ -283,6 +284,7 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
 template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_stream(LinearArgs a) {
+    enter_group<MODE>(a);
     constexpr int KS = BK / 16;                       // MFMA K steps per slice
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -554,7 +556,8 @@ static const void* stream_fn(int mode) {
 static hipError_t launch(const void* fn, const LinearArgs& a, int threads, hipStream_t stream) {
     LinearArgs args = a;
     void* params[] = {&args};
-    return hipLaunchKernel(fn, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(threads), params, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)a.groups), dim3(threads), params,
+                           0, stream);
 }
 
 template <int E>

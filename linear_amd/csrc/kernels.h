@@ -49,6 +49,23 @@ constexpr int kSkinnyTile = 16;
 constexpr int kSkinnyKStep = 32;
 hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream);
 
+// Indexed contraction (x [M, K] against expert tables W [E, K, N], row m against
+// expert idx[m]): one workgroup per (expert, kIdxCols output columns).
+struct IndexedArgs {
+    const uint16_t* x;      // [M, K], row stride ldx
+    const uint16_t* w;      // [E, K, N]: k-row stride ldw, expert stride sw
+    const int32_t* idx;     // [M]
+    void* y;                // [M, N], row stride ldy (16-bit words or floats)
+    int64_t ldx, ldw, sw, ldy;
+    int E, M, N, K;
+    int vec_x;              // x rows load as 16-byte fragments
+    int vec_store;          // y takes 4-element vector stores
+};
+constexpr int kIdxWaves = 4;
+constexpr int kIdxCols = 64;
+constexpr int kIdxCap = 320;   // rows collected per batch
+hipError_t launch_indexed(int elem, const IndexedArgs& a, int mode, hipStream_t stream);
+
 // The activation tables of element type elem on `device` (3 x kActWords words:
 // SiLU, tanh GeLU, erf GeLU), built on `stream` by the first call and waited for
 // there; that first call fails with hipErrorStreamCaptureUnsupported under

@@ -49,7 +49,15 @@ struct Request {
     int elem;        // lin::kF16 or lin::kBF16
     bool f32_out;    // y holds the unrounded FP32 sums
     const linear_epilogue* epi = nullptr;   // the epilogue entry points: the program
+    int64_t G = 1, sx = 0, sy = 0;           // grouped calls: groups, x and y group strides
 };
+
+// The byte range of G groups of a [rows, cols] matrix (row stride ld, group stride s).
+Extent extent_g(const void* p, int64_t G, int64_t s, int64_t rows, int64_t ld, int64_t cols, int64_t eb = 2) {
+    Extent e{(uintptr_t)p, (uintptr_t)p};
+    if (p && G > 0 && rows > 0 && cols > 0) e.hi = e.lo + (uintptr_t)(((G - 1) * s + (rows - 1) * ld + cols) * eb);
+    return e;
+}
 
 bool epi_uses(const linear_epilogue* ep, int32_t op) {
     for (int s = 0; s < ep->nsteps; ++s)
@@ -89,20 +97,27 @@ int32_t validate_epilogue(const Request& r) {
 
 // Shape, pointer, stride, alias and path checks.  Pure host logic.
 int32_t validate(const Request& r) {
-    if (r.M < 0 || r.N < 0 || r.K < 0) return LINEAR_E_SHAPE;
-    if (r.M > kMaxDim || r.N > kMaxDim || r.K > kMaxDim) return LINEAR_E_SHAPE;
+    if (r.M < 0 || r.N < 0 || r.K < 0 || r.G < 0) return LINEAR_E_SHAPE;
+    if (r.M > kMaxDim || r.N > kMaxDim || r.K > kMaxDim || r.G > kMaxGridY) return LINEAR_E_SHAPE;
+    if (r.G > 1 && r.N * r.G > kMaxDim) return LINEAR_E_SHAPE;
     if (r.path != LINEAR_PATH_AUTO && r.path != LINEAR_PATH_GEMM && r.path != LINEAR_PATH_SKINNY)
         return LINEAR_E_PATH;
-    if (r.M == 0 || r.N == 0) return LINEAR_OK;  // nothing to write
+    if (r.M == 0 || r.N == 0 || r.G == 0) return LINEAR_OK;  // nothing to write
     if (!r.y) return LINEAR_E_NULL;
     if (r.K > 0 && (!r.x || !r.w)) return LINEAR_E_NULL;
     if (r.need_bias && !r.b) return LINEAR_E_NULL;
     if (r.ldx < r.K || r.ldw < r.K || r.ldy < r.N) return LINEAR_E_STRIDE;
     if (r.ldx > kMaxLdIn || r.ldw > kMaxLdIn || r.ldy > kMaxLdOut) return LINEAR_E_STRIDE;
-    const Extent ey = extent(r.y, r.M, r.ldy, r.N, r.f32_out ? 4 : 2);
-    if (overlaps(ey, extent(r.x, r.M, r.ldx, r.K))) return LINEAR_E_ALIAS;
-    if (overlaps(ey, extent(r.w, r.N, r.ldw, r.K))) return LINEAR_E_ALIAS;
-    if (r.b && overlaps(ey, extent(r.b, 1, r.N, r.N))) return LINEAR_E_ALIAS;
+    if (r.G > 1) {
+        // groups read their activation slices anywhere, but write disjoint outputs
+        if (r.sx < 0 || r.sx > kMaxLdOut * 1024) return LINEAR_E_STRIDE;
+        if (r.sy < (r.M - 1) * r.ldy + r.N || r.sy > kMaxLdOut * 1024) return LINEAR_E_STRIDE;
+    }
+    const int64_t eb = r.f32_out ? 4 : 2;
+    const Extent ey = extent_g(r.y, r.G, r.sy, r.M, r.ldy, r.N, eb);
+    if (overlaps(ey, extent_g(r.x, r.G, r.sx, r.M, r.ldx, r.K))) return LINEAR_E_ALIAS;
+    if (overlaps(ey, extent(r.w, r.N * r.G, r.ldw, r.K))) return LINEAR_E_ALIAS;
+    if (r.b && overlaps(ey, extent(r.b, 1, r.N * r.G, r.N * r.G))) return LINEAR_E_ALIAS;
     return LINEAR_OK;
 }
 
@@ -114,11 +129,11 @@ int32_t validate_all(const Request& r) {
 
 bool vector_loads_ok(const Request& r) {
     return ((uintptr_t)r.x % 16 == 0) && ((uintptr_t)r.w % 16 == 0) && (r.ldx % 8 == 0) &&
-           (r.ldw % 8 == 0) && (r.K % 8 == 0);
+           (r.ldw % 8 == 0) && (r.K % 8 == 0) && (r.G <= 1 || r.sx % 8 == 0);
 }
 
 bool vector_store_ok(const Request& r) {
-    return ((uintptr_t)r.y % (r.f32_out ? 16 : 8) == 0) && (r.ldy % 4 == 0);
+    return ((uintptr_t)r.y % (r.f32_out ? 16 : 8) == 0) && (r.ldy % 4 == 0) && (r.G <= 1 || r.sy % 4 == 0);
 }
 
 // Tile choice for the register-staged kernel (unaligned layouts, not tuned): the
@@ -170,7 +185,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         p->threads = lin::kSkinnyWaves * 64;
         const int64_t gx = (r.N + 15) / 16, gy = (r.M + 15) / 16;
         if (gx > kMaxGridX || gy > kMaxGridY) return LINEAR_E_SHAPE;
-        p->grid = gx * gy;
+        p->grid = gx * gy * r.G;
     } else {
         const bool stream = p->vector_io != 0;
         const int c = stream ? choose_stream_config(r.M, r.N) : choose_gemm_config(r.M, r.N);
@@ -181,6 +196,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         p->threads = g.wm * g.wn * 64;
         p->grid = ((r.M + g.bm - 1) / g.bm) * ((r.N + g.bn - 1) / g.bn);
         if (p->grid > kMaxGridX / 64) return LINEAR_E_SHAPE;
+        p->grid *= r.G;
     }
     return LINEAR_OK;
 }
@@ -211,7 +227,7 @@ int32_t check_device(int* dev_out) {
 int32_t run(const Request& r, void* stream) {
     int32_t st = validate_all(r);
     if (st != LINEAR_OK) return st;
-    if (r.M == 0 || r.N == 0) return LINEAR_OK;
+    if (r.M == 0 || r.N == 0 || r.G == 0) return LINEAR_OK;
     linear_plan p;
     st = plan(r, &p);
     if (st != LINEAR_OK) return st;
@@ -231,10 +247,14 @@ int32_t run(const Request& r, void* stream) {
     a.N = (int)r.N;
     a.K = (int)r.K;
     a.vec_store = vector_store_ok(r) ? 1 : 0;
+    a.groups = (int)r.G;
+    a.gsx = r.sx;
+    a.gsy = r.sy;
     memset(&a.epi, 0, sizeof a.epi);
     auto al16 = [](const void* q, int64_t ld) { return ((uintptr_t)q % 16 == 0) && (ld % 8 == 0); };
     // 16-byte row accesses of the staged epilogue: y and the bias (the program's inputs below)
-    a.epi.vec16 = (al16(r.y, r.ldy) ? 1 : 0) | (al16(r.b, 8) ? 2 : 0);
+    a.epi.vec16 = (al16(r.y, r.ldy) && (r.G <= 1 || r.sy % 8 == 0) ? 1 : 0) |
+                  (al16(r.b, 8) && (r.G <= 1 || r.N % 8 == 0) ? 2 : 0);
     int mode = r.f32_out ? lin::kOutF32 : (r.b != nullptr ? lin::kOutBias : lin::kOutRound);
     if (r.epi) {
         mode = lin::kOutEpi;
@@ -286,9 +306,75 @@ int32_t run(const Request& r, void* stream) {
     return LINEAR_OK;
 }
 
+// The indexed contraction: checks, then one launch.
+int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                    int64_t sw, const int32_t* idx, void* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                    int64_t K, void* stream) {
+    if (M < 0 || N < 0 || K < 0 || E < 0) return LINEAR_E_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || E > kMaxGridY) return LINEAR_E_SHAPE;
+    if (M == 0 || N == 0 || E == 0) return LINEAR_OK;   // no row has an expert: nothing to write
+    if (!y || !idx) return LINEAR_E_NULL;
+    if (K > 0 && (!x || !w)) return LINEAR_E_NULL;
+    if (ldx < K || ldw < N || ldy < N || sw < K * ldw) return LINEAR_E_STRIDE;
+    if (ldx > kMaxLdOut || ldw > kMaxLdOut || ldy > kMaxLdOut) return LINEAR_E_STRIDE;
+    const int64_t eb = f32_out ? 4 : 2;
+    const Extent ey = extent(y, M, ldy, N, eb);
+    if (overlaps(ey, extent(x, M, ldx, K))) return LINEAR_E_ALIAS;
+    if (K > 0 && overlaps(ey, extent_g(w, E, sw, K, ldw, N))) return LINEAR_E_ALIAS;
+    if (overlaps(ey, extent(idx, 1, M, M, 4))) return LINEAR_E_ALIAS;
+    int dev = 0;
+    int32_t st = check_device(&dev);
+    if (st != LINEAR_OK) return st;
+    lin::IndexedArgs a;
+    a.x = x;
+    a.w = w;
+    a.idx = idx;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldw = ldw;
+    a.sw = sw;
+    a.ldy = ldy;
+    a.E = (int)E;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.vec_x = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0) ? 1 : 0;
+    a.vec_store = ((uintptr_t)y % (f32_out ? 16 : 8) == 0) && (ldy % 4 == 0) ? 1 : 0;
+    const hipError_t e = lin::launch_indexed(elem, a, f32_out ? lin::kOutF32 : lin::kOutRound, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int32_t)e;
+        return LINEAR_E_LAUNCH;
+    }
+    return LINEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t linear_f16_indexed(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                           const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                           int64_t K, void* stream) {
+    return run_indexed(lin::kF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+}
+
+int32_t linear_bf16_indexed(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                            const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                            int64_t K, void* stream) {
+    return run_indexed(lin::kBF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+}
+
+int32_t linear_f16_indexed_f32out(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                                  const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                                  int64_t K, void* stream) {
+    return run_indexed(lin::kF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+}
+
+int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                                   const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                                   int64_t K, void* stream) {
+    return run_indexed(lin::kBF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+}
 
 int32_t linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
                    const uint16_t* b, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
@@ -357,6 +443,34 @@ int32_t linear_bf16_epilogue(const uint16_t* x, int64_t ldx, const uint16_t* wei
                              int64_t K, int32_t path, void* stream) {
     if (!epilogue) return LINEAR_E_NULL;
     Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kBF16, false, epilogue};
+    return run(r, stream);
+}
+
+int32_t linear_f16_grouped(const uint16_t* x, int64_t ldx, int64_t sx, const uint16_t* weight, int64_t ldw,
+                           const uint16_t* b, uint16_t* y, int64_t ldy, int64_t sy, int64_t G, int64_t M,
+                           int64_t N, int64_t K, int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false, lin::kF16, false, nullptr, G, sx, sy};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_grouped(const uint16_t* x, int64_t ldx, int64_t sx, const uint16_t* weight, int64_t ldw,
+                            const uint16_t* b, uint16_t* y, int64_t ldy, int64_t sy, int64_t G, int64_t M,
+                            int64_t N, int64_t K, int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, b, y, ldy, M, N, K, path, false, lin::kBF16, false, nullptr, G, sx, sy};
+    return run(r, stream);
+}
+
+int32_t linear_f16_grouped_f32out(const uint16_t* x, int64_t ldx, int64_t sx, const uint16_t* weight, int64_t ldw,
+                                  float* y, int64_t ldy, int64_t sy, int64_t G, int64_t M, int64_t N, int64_t K,
+                                  int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kF16, true, nullptr, G, sx, sy};
+    return run(r, stream);
+}
+
+int32_t linear_bf16_grouped_f32out(const uint16_t* x, int64_t ldx, int64_t sx, const uint16_t* weight,
+                                   int64_t ldw, float* y, int64_t ldy, int64_t sy, int64_t G, int64_t M, int64_t N,
+                                   int64_t K, int32_t path, void* stream) {
+    Request r{x, ldx, weight, ldw, nullptr, y, ldy, M, N, K, path, false, lin::kBF16, true, nullptr, G, sx, sy};
     return run(r, stream);
 }
 

@@ -35,6 +35,7 @@ namespace lin {
 template <int WAVES, int E, int MODE>
 __global__ void __launch_bounds__(WAVES * 64)
 skinny_stream(LinearArgs a) {
+    enter_group<MODE>(a);
     constexpr int PU = 16;                    // MFMA steps (32 K values each) per pass
     constexpr int XPITCH = PU * 64 + 16;      // bytes per LDS row of x: 512 halves + pad
     __shared__ __attribute__((aligned(16))) unsigned char xs[WAVES * 16 * XPITCH];
@@ -116,6 +117,7 @@ skinny_stream(LinearArgs a) {
 template <int WAVES, int E, int MODE>
 __global__ void __launch_bounds__(WAVES * 64)
 skinny_kernel(LinearArgs a) {
+    enter_group<MODE>(a);
     constexpr int UNROLL = 8;
     const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -187,7 +189,7 @@ static const void* skinny_fn(bool vec, int mode) {
 }
 
 hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
+    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16), (unsigned)a.groups);
     const dim3 block(kSkinnyWaves * 64);
     LinearArgs args = a;
     void* params[] = {&args};

@@ -57,6 +57,71 @@ WORKLOADS = {
                      "deep-K down-projection, M and N not multiples of a tile"),
 }
 
+# Grouped and indexed contractions ("The Graph IR", op table: GroupedDenseContraction,
+# IndexedMatMul).  The pages give no shapes; these are a grouped projection of the
+# same 4096-wide model and mixture-of-experts feed-forward shapes (8 experts,
+# top-2 routing: 16 decode tokens -> 32 rows, 2048 prefill tokens -> 4096 rows).
+@dataclass(frozen=True)
+class GroupedWorkload:
+    name: str
+    G: int
+    M: int
+    N: int
+    K: int
+    a: float
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.G * self.M * self.N * self.K
+
+    @property
+    def bytes(self) -> int:
+        return 2 * (self.G * self.M * self.K + self.G * self.N * self.K + self.G * self.N + self.G * self.M * self.N)
+
+
+@dataclass(frozen=True)
+class IndexedWorkload:
+    name: str
+    E: int
+    M: int
+    N: int
+    K: int
+    a: float
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+GROUPED = {"grouped": GroupedWorkload("grouped", 8, 512, 4096, 4096, 1.0 / 64.0)}
+INDEXED = {
+    "moe_decode": IndexedWorkload("moe_decode", 8, 32, 4096, 4096, 1.0 / 64.0),
+    "moe_prefill": IndexedWorkload("moe_prefill", 8, 4096, 4096, 4096, 1.0 / 64.0),
+}
+
+
+def make_grouped_inputs(G: int, M: int, N: int, K: int, a: float, seed: int = 0, device: str = "cpu",
+                        dtype: torch.dtype = torch.float16):
+    """x [G, M, K] ~ N(0,1), weight [G*N, K] and b [G*N] ~ U(-a, a), drawn in that order."""
+    x, w, b = make_inputs(G * M, G * N, K, a, seed=seed, device=device, dtype=dtype)
+    return x.reshape(G, M, K), w, b
+
+
+def make_indexed_inputs(E: int, M: int, N: int, K: int, a: float, seed: int = 0, device: str = "cpu",
+                        dtype: torch.dtype = torch.float16):
+    """x [M, K] ~ N(0,1), expert tables w [E, K, N] ~ U(-a, a), idx [M] uniform over the
+    experts (int32), drawn in that order."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn((M, K), generator=g, dtype=torch.float32)
+    w = torch.rand((E, K, N), generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0).mul_(a)
+    idx = torch.randint(0, max(E, 1), (M,), generator=g, dtype=torch.int64).to(torch.int32)
+    x, w = x.to(dtype), w.to(dtype)
+    if device != "cpu":
+        x, w, idx = x.to(device), w.to(device), idx.to(device)
+    return x, w, idx
+
+
 # The decode batch: one step runs both decode shapes over the same weight size.
 DECODE_STEP = ("gemv1", "gemv16")
 

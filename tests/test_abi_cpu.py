@@ -157,6 +157,72 @@ def test_epilogue_unused_inputs_may_be_null_and_in_place_residual_is_accepted():
     assert la._lib().linear_f16_epilogue(X, 64, W, 64, None, Y, 32, 8, 32, 64, 0, None) == la.LINEAR_E_NULL
 
 
+def call_grouped(x=X, ldx=64, sx=8 * 64, w=W, ldw=64, b=B, y=Y, ldy=32, sy=8 * 32, G=3, M=8, N=32, K=64,
+                 path=0):
+    return la._lib().linear_f16_grouped(x, ldx, sx, w, ldw, b, y, ldy, sy, G, M, N, K, path, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=-1), la.LINEAR_E_SHAPE),
+    (dict(G=65536), la.LINEAR_E_SHAPE),
+    (dict(sy=7 * 32 + 31), la.LINEAR_E_STRIDE),      # groups would write overlapping outputs
+    (dict(sx=-1), la.LINEAR_E_STRIDE),
+    (dict(y=X + 2 * 64 * 8 * 2), la.LINEAR_E_ALIAS),  # y inside the third activation slice
+    (dict(b=Y + 2 * 8 * 32 * 2), la.LINEAR_E_ALIAS),  # b inside the third output group
+    (dict(path=9), la.LINEAR_E_PATH),
+    (dict(x=0), la.LINEAR_E_NULL),
+])
+def test_grouped_validation(kw, code):
+    assert call_grouped(**kw) == code
+
+
+@needs_lib
+def test_grouped_noops_and_device_check():
+    assert call_grouped(G=0, x=0, w=0, y=0) == la.LINEAR_OK
+    rc = call_grouped(sx=0)             # every group reading the same activation is allowed
+    assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
+    if not torch.cuda.is_available():
+        assert rc == la.LINEAR_E_DEVICE
+
+
+I = 0x7F6000000000   # fake idx
+
+
+def call_indexed(x=X, ldx=64, w=W, ldw=32, sw=64 * 32, idx=I, y=Y, ldy=32, E=4, M=8, N=32, K=64, f32=False):
+    fn = la._lib().linear_f16_indexed_f32out if f32 else la._lib().linear_f16_indexed
+    return fn(x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("f32", [False, True], ids=["round", "f32out"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=-1), la.LINEAR_E_SHAPE),
+    (dict(E=65536), la.LINEAR_E_SHAPE),
+    (dict(M=-2), la.LINEAR_E_SHAPE),
+    (dict(idx=0), la.LINEAR_E_NULL),
+    (dict(w=0), la.LINEAR_E_NULL),
+    (dict(ldw=31), la.LINEAR_E_STRIDE),
+    (dict(sw=64 * 32 - 1), la.LINEAR_E_STRIDE),
+    (dict(ldx=63), la.LINEAR_E_STRIDE),
+    (dict(ldy=31), la.LINEAR_E_STRIDE),
+    (dict(y=W + 3 * 64 * 32 * 2), la.LINEAR_E_ALIAS),   # y inside the last expert table
+    (dict(idx=Y + 16), la.LINEAR_E_ALIAS),
+])
+def test_indexed_validation(kw, code, f32):
+    assert call_indexed(f32=f32, **kw) == code
+
+
+@needs_lib
+def test_indexed_noops_and_device_check():
+    assert call_indexed(E=0, x=0, w=0, idx=0, y=0) == la.LINEAR_OK
+    assert call_indexed(M=0, idx=0) == la.LINEAR_OK
+    rc = call_indexed()
+    assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
+    if not torch.cuda.is_available():
+        assert rc == la.LINEAR_E_DEVICE
+
+
 def plan(M, N, K, path=0, x=X, w=W, ldx=None, ldw=None):
     p = la._Plan()
     rc = la._lib().linear_f16_plan(x, ldx or K, w, ldw or K, B, Y, N, M, N, K, path, ctypes.byref(p))

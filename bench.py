@@ -325,9 +325,11 @@ def bench_indexed(name, torch, la, workloads, stream, calls, dtype_name="f16"):
     ws = [w] + [w.clone() for _ in range(sets - 1)]
     ys = [torch.empty((wl.M, wl.N), dtype=dtype, device="cuda") for _ in range(sets)]
 
+    work = torch.empty(la.indexed_workspace_bytes(wl.E, wl.M), dtype=torch.uint8, device="cuda")
+
     def call(i):
         k = i % sets
-        fn(x, ws[k], idx, out=ys[k], stream=stream)
+        fn(x, ws[k], idx, out=ys[k], stream=stream, workspace=work)
 
     graph = capture(call, sets, stream, torch)
     replays = max(1, calls // sets)

@@ -58,6 +58,7 @@ extern "C" {
 #define LINEAR_E_LAUNCH   7  /* a kernel launch failed; linear_last_hip_error() has the HIP code */
 #define LINEAR_E_EPILOGUE 8  /* epilogue program: step count outside 0..LINEAR_EPI_MAX_STEPS or an unknown step */
 #define LINEAR_E_CAPTURE  9  /* the first activation epilogue on a device was called under stream capture */
+#define LINEAR_E_WORKSPACE 10 /* indexed contraction: workspace misaligned or below linear_indexed_workspace_bytes */
 
 /* Path selectors for linear_f16_ex / linear_f16_plan. */
 #define LINEAR_PATH_AUTO   0  /* M <= 16: skinny path; otherwise the MFMA tiled GEMM */
@@ -271,33 +272,42 @@ int32_t linear_bf16_grouped_f32out(const uint16_t* x, int64_t ldx, int64_t sx,
  * whose idx lies outside [0, E) has no expert and its outputs are left untouched.
  * Only rows m < M and columns n < N are written; reruns are bit-identical.
  * E up to 65535; M, N, K < 2^31.  The _f32out forms store the unrounded sums.
- * Errors as for linear_f16_ex (y overlapping x, w or idx is LINEAR_E_ALIAS);
- * E == 0, M == 0 or N == 0 is a successful no-op.
+ *
+ * workspace: device memory of at least linear_indexed_workspace_bytes(E, M)
+ * bytes, 16-byte aligned, owned by the caller, overwritten by the call (it holds
+ * the row-to-expert binning) and free again once the call's work on `stream`
+ * has finished; two calls in flight at once need two workspaces.
+ *
+ * Errors as for linear_f16_ex (y or the workspace overlapping x, w, idx or each
+ * other is LINEAR_E_ALIAS; a NULL workspace is LINEAR_E_NULL, a short or
+ * misaligned one LINEAR_E_WORKSPACE); E == 0, M == 0 or N == 0 is a successful
+ * no-op that touches nothing.
  */
+int64_t linear_indexed_workspace_bytes(int64_t E, int64_t M);   /* -1 if E or M is out of range */
 int32_t linear_f16_indexed(const uint16_t* x, int64_t ldx,
                            const uint16_t* w, int64_t ldw, int64_t sw,
                            const int32_t* idx,
                            uint16_t* y, int64_t ldy,
                            int64_t E, int64_t M, int64_t N, int64_t K,
-                           void* stream);
+                           void* workspace, int64_t workspace_bytes, void* stream);
 int32_t linear_bf16_indexed(const uint16_t* x, int64_t ldx,
                             const uint16_t* w, int64_t ldw, int64_t sw,
                             const int32_t* idx,
                             uint16_t* y, int64_t ldy,
                             int64_t E, int64_t M, int64_t N, int64_t K,
-                            void* stream);
+                            void* workspace, int64_t workspace_bytes, void* stream);
 int32_t linear_f16_indexed_f32out(const uint16_t* x, int64_t ldx,
                                   const uint16_t* w, int64_t ldw, int64_t sw,
                                   const int32_t* idx,
                                   float* y, int64_t ldy,
                                   int64_t E, int64_t M, int64_t N, int64_t K,
-                                  void* stream);
+                                  void* workspace, int64_t workspace_bytes, void* stream);
 int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx,
                                    const uint16_t* w, int64_t ldw, int64_t sw,
                                    const int32_t* idx,
                                    float* y, int64_t ldy,
                                    int64_t E, int64_t M, int64_t N, int64_t K,
-                                   void* stream);
+                                   void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Which kernel a call would launch.  Pure host function: touches no device. */
 typedef struct linear_plan {

@@ -26,6 +26,7 @@ LINEAR_E_DEVICE = 6
 LINEAR_E_LAUNCH = 7
 LINEAR_E_EPILOGUE = 8
 LINEAR_E_CAPTURE = 9
+LINEAR_E_WORKSPACE = 10
 
 # Epilogue steps (include/linear_amd.h, LINEAR_EPI_*)
 EPI_MAX_STEPS = 8
@@ -44,6 +45,7 @@ ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_
                 "linear_bf16", "linear_bf16_nobias", "linear_bf16_ex", "linear_bf16_f32out",
                 "linear_f16_epilogue", "linear_bf16_epilogue",
                 "linear_f16_grouped", "linear_bf16_grouped", "linear_f16_grouped_f32out", "linear_bf16_grouped_f32out",
+                "linear_indexed_workspace_bytes",
                 "linear_f16_indexed", "linear_bf16_indexed", "linear_f16_indexed_f32out", "linear_bf16_indexed_f32out",
                 "linear_f16_plan", "linear_status_string", "linear_last_hip_error")
 
@@ -113,8 +115,10 @@ def _lib():
         getattr(lib, name).restype = i32
     for name in ("linear_f16_indexed", "linear_bf16_indexed", "linear_f16_indexed_f32out",
                  "linear_bf16_indexed_f32out"):
-        getattr(lib, name).argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64, vp]
+        getattr(lib, name).argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp]
         getattr(lib, name).restype = i32
+    lib.linear_indexed_workspace_bytes.argtypes = [i64, i64]
+    lib.linear_indexed_workspace_bytes.restype = i64
     lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
                                     ctypes.POINTER(_Plan)]
     lib.linear_f16_plan.restype = i32
@@ -361,7 +365,15 @@ def linear_bf16_grouped_f32out(x, weight, out=None, path: int = PATH_AUTO, strea
     return _grouped_call(torch.bfloat16, x, weight, None, out, True, path, stream)
 
 
-def _indexed_call(dtype, x, w, idx, out, f32, stream):
+def indexed_workspace_bytes(E: int, M: int) -> int:
+    """Bytes of device workspace an indexed call with E experts and M rows needs."""
+    n = _lib().linear_indexed_workspace_bytes(E, M)
+    if n < 0:
+        raise ValueError("E=%d, M=%d out of range" % (E, M))
+    return n
+
+
+def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
     """x [M, K], w [E, K, N] (inner two dims row-major), idx [M] int32."""
     if x.dtype != dtype or w.dtype != dtype:
         raise TypeError("x and w must be %s" % dtype)
@@ -384,30 +396,36 @@ def _indexed_call(dtype, x, w, idx, out, f32, stream):
     yp, ldy = _mat(out, "out", out_dtype)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [%d, %d]" % (M, N))
+    need = indexed_workspace_bytes(E, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    elif workspace.dtype != torch.uint8 or workspace.dim() != 1 or workspace.numel() < need:
+        raise ValueError("workspace must be a uint8 tensor of at least %d bytes" % need)
     tag = "bf16" if dtype == torch.bfloat16 else "f16"
     name = "linear_%s_indexed%s" % (tag, "_f32out" if f32 else "")
     rc = getattr(_lib(), name)(xp, ldx, w.data_ptr(), ldw, sw, idx.data_ptr(), yp, ldy, E, M, N, K,
-                               _stream_handle(stream, x, out))
+                               workspace.data_ptr(), workspace.numel(), _stream_handle(stream, x, out))
     _check(rc, name)
     return out
 
 
-def linear_f16_indexed(x, w, idx, out=None, stream=None):
+def linear_f16_indexed(x, w, idx, out=None, stream=None, workspace=None):
     """Indexed contraction: row m of x against expert table w[idx[m]] ([K, N]); rows whose
-    idx has no expert keep out's contents."""
-    return _indexed_call(torch.float16, x, w, idx, out, False, stream)
+    idx has no expert keep out's contents.  workspace: a uint8 device tensor of at least
+    indexed_workspace_bytes(E, M) bytes (allocated per call when None)."""
+    return _indexed_call(torch.float16, x, w, idx, out, False, stream, workspace)
 
 
-def linear_bf16_indexed(x, w, idx, out=None, stream=None):
-    return _indexed_call(torch.bfloat16, x, w, idx, out, False, stream)
+def linear_bf16_indexed(x, w, idx, out=None, stream=None, workspace=None):
+    return _indexed_call(torch.bfloat16, x, w, idx, out, False, stream, workspace)
 
 
-def linear_f16_indexed_f32out(x, w, idx, out=None, stream=None):
-    return _indexed_call(torch.float16, x, w, idx, out, True, stream)
+def linear_f16_indexed_f32out(x, w, idx, out=None, stream=None, workspace=None):
+    return _indexed_call(torch.float16, x, w, idx, out, True, stream, workspace)
 
 
-def linear_bf16_indexed_f32out(x, w, idx, out=None, stream=None):
-    return _indexed_call(torch.bfloat16, x, w, idx, out, True, stream)
+def linear_bf16_indexed_f32out(x, w, idx, out=None, stream=None, workspace=None):
+    return _indexed_call(torch.bfloat16, x, w, idx, out, True, stream, workspace)
 
 
 def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,

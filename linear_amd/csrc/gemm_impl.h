@@ -14,7 +14,7 @@
 //    accumulator rows are output columns n: each lane ends up holding four
 //    consecutive n of one output row m and stores them as one 8-byte write.
 //  - Both operands are K-contiguous in HBM and are read in place ([N, K] weight,
-//    no transpose copy, as the poot op table's dense contraction requires):
+//    no transpose copy, as the op table's dense contraction requires):
 //    each thread moves 16-byte chunks along K; a wave covers 8 full 128-byte
 //    rows per load instruction.
 //  - K-slices of BK = 64 are staged through LDS, double buffered: the loads of
@@ -36,23 +36,10 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "sched.h"
 
 namespace lin {
 
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int G = tiles_m * tiles_n;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int q = G >> 3, r = G & 7;
-    const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-    constexpr int GROUP = 8;
-    const int per_group = GROUP * tiles_n;
-    const int g = t / per_group;
-    const int first_m = g * GROUP;
-    const int gm = min(tiles_m - first_m, GROUP);
-    const int rem = t - g * per_group;
-    tm = first_m + rem % gm;
-    tn = rem / gm;
-}
 
 // Register-staged variant for layouts the streaming kernel cannot take (K, ldx or
 // ldw not a multiple of 8, or x / weight not 16-byte aligned): every element is
@@ -165,30 +152,6 @@ gemm_kernel(LinearArgs a) {
         }
 }
 
-// Calls f.template operator()<I>() for I = B .. N-1 (compile-time loop).
-template <int B, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < N) {
-        f.template operator()<B>();
-        static_for<B + 1, N>(f);
-    }
-}
-
-// Instruction order of one K step of the streaming GEMM: its first MFMA, the
-// NREAD fragment reads of the next step, then the other NMFMA - 1 MFMAs with ND
-// loads spaced evenly between them.
-template <int NMFMA, int NREAD, int ND>
-__device__ __forceinline__ void order_step() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (NREAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-    constexpr int q = (NMFMA - 1) / (ND + 1);
-    static_for<0, ND>([&]<int d>() {
-        if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x008, q, 0);
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    });
-    if constexpr (NMFMA - 1 - q * ND > 0) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - 1 - q * ND, 0);
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // The epilogue program over a tile of rounded projection words staged in LDS.
 // Layout: row r of the BM x BN tile holds CPR = BN / 8 chunks of 16 bytes, chunk

@@ -3,21 +3,30 @@
 // row m contracts against expert idx[m], y[m, n] = sum_k x[m, k] * W[idx[m], k, n],
 // FP32 accumulation, the result rounded to the element type (or the FP32 sums).
 //
-// One workgroup per (expert, 64 output columns).  It first collects, in index
-// order, the rows whose idx names its expert: the 256 threads test 256 entries
-// of idx at a time and place the hits with wave ballots and per-wave counts, so
-// the row list is deterministic and needs no workspace.  The rows are then
-// contracted 16 at a time with v_mfma_f32_16x16x32 (expert columns as the A
-// operand, x rows as B), K split over the 4 waves and the partial tiles added in
-// FP32 through LDS in wave order.  Each expert's table is therefore read once
-// per 16 of its rows, and an expert no row selects costs one scan of idx.
+// Two paths.
 //
-// The expert table is stored k-major ([K, N], n contiguous) while an MFMA
-// operand holds 8 consecutive k of one n per lane, so the A fragments are
-// gathered column-wise: lane l takes W[k .. k+7][n0 + l % 16].  x rows are
-// K-contiguous and load as 16-byte fragments when aligned.
+// Routed (16-byte aligned layouts).  A routing pass (one workgroup) counts the
+// rows of each expert, lays out the row list expert by expert and cuts it into
+// row tiles of at most BM rows: the tile table.  The contraction kernel then runs
+// one workgroup per (tile, BN output columns), a GEMM over the tile's gathered x
+// rows and the expert's [K, BN] column panel, streamed through an LDS ring by
+// direct-to-LDS loads, 64 k per slice.  The table is k-major ([K, N], n
+// contiguous) while an MFMA operand holds 8 consecutive k per lane, so the
+// panel is read out of LDS with the transposing read ds_read_b64_tr_b16: within
+// each 16-lane group it hands lane i the 4 elements that lanes 4j + i/4 (j = 0..3)
+// address at their offset i % 4, so when the lanes address 4 k-rows x 16 columns
+// in 8-byte pieces, lane i receives 4 consecutive k of column i.  The output rows
+// are independent, so the order of rows inside a tile (set by the routing pass's
+// atomic slots) does not change any result.
+//
+// Row scan (any other layout).  One workgroup per (expert, 64 output columns)
+// collects, in index order, the rows whose idx names its expert (ballots and
+// per-wave counts) and contracts them 16 at a time with v_mfma_f32_16x16x32,
+// the A fragments gathered column-wise from the table, K split over the 4 waves
+// and the partial tiles added in FP32 through LDS in wave order.
 #include "common.h"
 #include "kernels.h"
+#include "sched.h"
 
 namespace lin {
 
@@ -137,6 +146,566 @@ indexed_kernel(IndexedArgs a) {
         }
         if (cursor >= a.M) break;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Routed path
+
+// Exclusive prefix sum of v over the 1024 threads; *total gets the sum.  Uses
+// wsum (16 words) and ends with a barrier.
+__device__ inline int block_scan_1024(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int s = lane < 16 ? wsum[lane] : 0;
+        int si = s;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int t = __shfl_up(si, o, 64);
+            if (lane >= o) si += t;
+        }
+        if (lane < 16) wsum[16 + lane] = si - s;   // exclusive wave offsets
+        if (lane == 15) wsum[32] = si;
+    }
+    __syncthreads();
+    const int r = wsum[16 + wave] + incl - v;
+    *total = wsum[32];
+    __syncthreads();
+    return r;
+}
+
+// The routing pass: tile count, row list and tile table into the workspace.
+// Row list: the rows of expert 0, then expert 1, ...; tile v = {first list
+// position, expert, rows (<= BM)}.
+__global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict__ idx, int M, int E, int BM,
+                                                      int32_t* __restrict__ ws) {
+    __shared__ int cnt[kIdxMaxExperts];
+    __shared__ int cur[kIdxMaxExperts];
+    __shared__ int tbase[kIdxMaxExperts];
+    __shared__ int wsum[48];
+    const int tid = threadIdx.x;
+    int32_t* perm = ws + kIdxHeaderWords;
+    int4* tiles = (int4*)(ws + idx_ws_tiles(M));
+
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    for (int m = tid; m < M; m += 1024) {
+        const int e = idx[m];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    // prefix sums over the experts of rows and of tiles: thread t owns experts 4t .. 4t+3
+    int c[4], rs = 0, ts = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        c[j] = e < E ? cnt[e] : 0;
+        rs += c[j];
+        ts += (c[j] + BM - 1) / BM;
+    }
+    int rtot, ttot;
+    int r0 = block_scan_1024(rs, wsum, &rtot);
+    int t0 = block_scan_1024(ts, wsum, &ttot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) {
+            cur[e] = r0;
+            tbase[e] = t0;
+        }
+        r0 += c[j];
+        t0 += (c[j] + BM - 1) / BM;
+    }
+    if (tid == 0) ws[0] = ttot;
+    __syncthreads();
+
+    // tile table: tile v belongs to the last expert whose first tile is <= v
+    for (int v = tid; v < ttot; v += 1024) {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tbase[mid] <= v) lo = mid;
+            else hi = mid - 1;
+        }
+        const int t = v - tbase[lo];
+        tiles[v] = make_int4(cur[lo] + t * BM, lo, min(BM, cnt[lo] - t * BM), 0);
+    }
+    __syncthreads();
+
+    // row list: each row takes the next free slot of its expert
+    for (int m = tid; m < M; m += 1024) {
+        const int e = idx[m];
+        if ((unsigned)e < (unsigned)E) perm[atomicAdd(&cur[e], 1)] = m;
+    }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The transposing LDS read at byte offset off of the workgroup's LDS.
+__device__ inline uint2 lds_read_tr16(const unsigned char* base, uint32_t off) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) unsigned char*)base + off));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Swizzle of the panel rows: the 32-byte column pair u of k-row kr sits at pair
+// u ^ pair_swz(kr).  The LDS serves a 64-lane 8-byte read 32 lanes at a time;
+// the 32 lanes of a transposing read address 32-byte pieces in the k-rows
+// kb + (0 .. 3) or kb + 8 + (0 .. 3) (kb a multiple of 16) and in two adjacent
+// pairs (32 x 32 fragments) or one pair of rows kb + (0 .. 3) and kb + 8 + (0 .. 3)
+// (16 x 16 fragments).  pair_swz takes 2 (kr % 4) + (kr / 8) % 2, so those eight
+// pieces land on eight different 32-byte bank groups either way: no conflicts.
+__host__ __device__ constexpr int pair_swz(int kr) { return 2 * (kr & 3) | ((kr >> 3) & 1); }
+
+// Workgroup (tile v, column tile tn): y[rows of v, n0 .. n0 + BN) for tile v's
+// expert.  Waves WM x WN; a wave owns TM = BM / WM rows and TN = BN / WN columns
+// as (TN / 32) x (TM / 32) blocks of v_mfma_f32_32x32x16 (panel columns as the
+// A operand, x rows as B).
+//
+// LDS slot of one 64-k slice: the panel, 64 k-rows of BN columns (2 BN bytes,
+// pair-swizzled as above), then BM x rows of 64 k (128 bytes, 16-byte chunk c
+// of row r at c ^ ((r >> 1) & 7), as in the dense kernel).  Each direct load
+// fills 1 KB of the slot; lane l lands at byte 16 l of it and fetches the chunk
+// that the swizzle places there.
+template <int BM, int BN, int WM, int WN, int STAGES, int E, int MODE>
+__global__ void __launch_bounds__(WM * WN * 64)
+indexed_routed(IndexedArgs a) {
+    constexpr int BK = 64, KS = BK / 16;
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int PROW = 2 * BN;                      // bytes per panel k-row
+    constexpr int PBYTES = BK * PROW;
+    constexpr int XBYTES = BM * BK * 2;
+    constexpr int SLICE = PBYTES + XBYTES;
+    constexpr int GP = PBYTES / 1024, GX = XBYTES / 1024;
+    constexpr int GPP = GP / NW, GPX = GX / NW;       // panel and x loads per wave per slice
+    constexpr int GPW = GPP + GPX;
+    static_assert(BN == 128 || BN == 256, "panel width must be 128 or 256 columns");
+    static_assert(BM % 32 == 0 && TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(GP % NW == 0 && GX % NW == 0, "direct loads must divide evenly over the waves");
+    static_assert(STAGES >= 2 && STAGES * SLICE <= 160 * 1024, "LDS ring too large");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
+
+    const int tiles_n = (a.N + BN - 1) / BN;
+    int tv, tn;
+    // column tile fastest: the used slots come first and fill every XCD evenly
+    // (consecutive workgroup ids are dealt round-robin over the 8 XCDs), and the
+    // tiles of one expert that share a column panel share an XCD when tiles_n
+    // is a multiple of 8
+    tv = blockIdx.x / tiles_n;
+    tn = blockIdx.x - tv * tiles_n;
+    if (tv >= a.ws[0]) return;                        // an unused slot (uniform)
+    const int4 tile = ((const int4*)(a.ws + idx_ws_tiles(a.M)))[tv];
+    const int32_t* list = a.ws + kIdxHeaderWords + tile.x;
+    const int expert = tile.y, rows = tile.z;
+    const int n0 = tn * BN;
+    const int K = a.K;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // the expert's table: K rows, the last one ending at column N
+    const __amdgpu_buffer_rsrc_t rp = matrix_rsrc(a.w + (int64_t)expert * a.sw, 0, K, a.ldw, a.N);
+    // all of x: M rows of K
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, 0, a.M, a.ldx, K);
+
+    // This wave's direct loads, per slice: panel groups wave * GPP + j (j < GPP),
+    // then x groups wave * GPX + j - GPP.
+    uint32_t goff[GPW];
+    int gk[GPW];                                      // k of the fetched chunk within a slice
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        if (j < GPP) {
+            const int byte = (wave * GPP + j) * 1024 + 16 * lane;
+            const int kr = byte / PROW;
+            const int c = ((byte % PROW) / 16) ^ (2 * pair_swz(kr));
+            const int n = n0 + 8 * c;
+            gk[j] = kr;
+            goff[j] = n < a.N ? (uint32_t)(((int64_t)kr * a.ldw + n) * 2) : kOOB;
+        } else {
+            const int xr = (wave * GPX + j - GPP) * 8 + lane / 8;
+            const int c = (lane % 8) ^ ((xr >> 1) & 7);
+            gk[j] = 8 * c;
+            goff[j] = xr < rows ? (uint32_t)(((int64_t)list[xr] * a.ldx + 8 * c) * 2) : kOOB;
+        }
+    }
+    const uint32_t pstep = (uint32_t)(BK * a.ldw * 2), xstep = (uint32_t)(BK * 2);
+    const int nk = (K + BK - 1) / BK;
+
+    const int wn = wave % WN, wm = wave / WN;
+    // transposing reads: lane (q = lane / 16, s = lane % 16) addresses k-row
+    // kq + s / 4 + (4h + 16 ks) and the 8-byte piece at column
+    // nb + 16 (q % 2) + 4 (s % 4) of its fragment; the piece's pair swizzle
+    // depends only on s / 4 and q / 2
+    const int q = lane >> 4, s = lane & 15;
+    const int kq = 8 * (q >> 1) + (s >> 2);
+    const int sw = pair_swz(kq);
+    uint32_t aoff[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+        const int n = wn * TN + i * 32 + 16 * (q & 1) + 4 * (s & 3);
+        aoff[i] = kq * PROW + (((n >> 3) ^ (2 * sw)) << 4) + 8 * ((n >> 2) & 1);
+    }
+    const int lr = lane & 31, lh = lane >> 5;
+    uint32_t boff[KS][FM];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int r = wm * TM + j * 32 + lr;
+            boff[ks][j] = PBYTES + r * 128 + (((ks * 2 + lh) ^ ((r >> 1) & 7)) << 4);
+        }
+
+#define LIN_IDX_ISSUE(t_, j_)                                                                    \
+    do {                                                                                         \
+        const int t__ = (t_);                                                                    \
+        unsigned char* slot__ = smem + (t__ % STAGES) * SLICE;                                   \
+        const bool kin__ = goff[(j_)] != kOOB && t__ * BK + gk[(j_)] < K;                        \
+        if ((j_) < GPP)                                                                          \
+            lds_dma16(rp, slot__ + (wave * GPP + (j_)) * 1024, kin__ ? goff[(j_)] + (uint32_t)t__ * pstep : kOOB); \
+        else                                                                                     \
+            lds_dma16(rx, slot__ + PBYTES + (wave * GPX + (j_) - GPP) * 1024,                    \
+                      kin__ ? goff[(j_)] + (uint32_t)t__ * xstep : kOOB);                        \
+    } while (0)
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
+
+    if (nk > 0) {
+        // as in the dense streaming kernel: loads past the last slice carry
+        // out-of-range offsets, so every wait below is static
+#pragma unroll
+        for (int t = 0; t < STAGES - 1; ++t)
+#pragma unroll
+            for (int j = 0; j < GPW; ++j) LIN_IDX_ISSUE(t, j);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
+        __syncthreads();
+
+        // The wave's work scales with the tile's rows: FA of its FM row blocks
+        // hold rows, and the reads and MFMAs of the others are skipped (one copy
+        // of the pipeline per FA; every copy issues the same loads and barriers).
+        auto pipeline = [&]<int FA>() {
+            u32x4 af[2][FN], bf[2][FM];
+            auto read_frags = [&](const unsigned char* slot, int ks, int buf) {
+                if constexpr (FA > 0) {
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) {
+                        const uint2 lo = lds_read_tr16(slot, aoff[i] + (16 * ks) * PROW);
+                        const uint2 hi = lds_read_tr16(slot, aoff[i] + (16 * ks + 4) * PROW);
+                        af[buf][i] = (u32x4){lo.x, lo.y, hi.x, hi.y};
+                    }
+#pragma unroll
+                    for (int j = 0; j < FA; ++j) bf[buf][j] = *(const u32x4*)(slot + boff[ks][j]);
+                }
+            };
+            auto mfmas = [&](int buf) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FA; ++j)
+                        acc[i][j] = mfma32x32x16<E>(af[buf][i], bf[buf][j], acc[i][j]);
+            };
+            read_frags(smem, 0, 0);
+
+            for (int t = 0; t < nk; ++t) {
+                // slice t + STAGES - 1 goes into the slot released by the barrier
+                // that ended slice t - 1
+#pragma unroll
+                for (int j = 0; j < GPW; ++j) LIN_IDX_ISSUE(t + STAGES - 1, j);
+                const unsigned char* slot = smem + (t % STAGES) * SLICE;
+                static_for<0, KS - 1>([&]<int ks>() {
+                    read_frags(slot, ks + 1, (ks + 1) & 1);
+                    mfmas(ks & 1);
+                    if constexpr (FA > 0) order_step<FN * FA, 2 * FN + FA, 0>();
+                });
+                // slice t + 1 has landed once only the later slices' loads are
+                // outstanding; the barrier also waits for every wave's reads of slot t
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
+                __syncthreads();
+                if (t + 1 < nk) read_frags(smem + ((t + 1) % STAGES) * SLICE, 0, KS & 1);
+                mfmas((KS - 1) & 1);
+            }
+        };
+        const int active = min(FM, max(0, (rows - wm * TM + 31) / 32));   // uniform
+        static_for<0, FM + 1>([&]<int fa>() {
+            if (active == fa) pipeline.template operator()<fa>();
+        });
+        // the zero-fill loads past the end must land before the LDS is released
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#undef LIN_IDX_ISSUE
+
+    // accumulator (i, j) element 4 b + r: panel column nb + 8 b + 4 (lane / 32) + r,
+    // tile row wm * TM + 32 j + lane % 32
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int tr = wm * TM + j * 32 + lr;
+        if (tr >= rows) continue;
+        const int m = list[tr];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int n = n0 + wn * TN + i * 32 + 8 * b + 4 * lh;
+                if (n < a.N)
+                    indexed_store4<E, MODE>(a, m, n,
+                                            (f32x4){acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
+                                                    acc[i][j][4 * b + 3]});
+            }
+    }
+}
+
+// Decode-shaped tiles (at most 16 rows): the contraction is the streaming of the
+// panel.  Workgroup (tile v, 128 columns); its 4 waves split K, wave w taking
+// the 32-k slices t = w, w + 4, ...: each streams its slices of the panel (32
+// k-rows x 256 bytes, 8 direct loads of four whole 256-byte row pieces) and of
+// the tile's x rows (16 rows x 64 bytes, 1 direct load) through a private ring
+// of S slots and waits only for its own loads, so the loop has no barrier.
+// v_mfma_f32_16x16x32: panel columns as A (two transposing reads per 16
+// columns), x rows as B.  At the end the 4 partial tiles are added in wave
+// order through LDS.
+//
+// Panel slot: k-row kr, 32-byte column pair u at pair u ^ pair_swz(kr).
+// x slot: row r (64 bytes), 16-byte chunk c at chunk c ^ ((r >> 2) & 3).
+// Exclusive prefix sum of v over the 256 threads; *total gets the sum.  Uses
+// wsum (8 words) and ends with a barrier.
+__device__ inline int block_scan_256(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Routing inside the workgroup, for small M: find tile v of the tile table the
+// routing pass would build (rows of each expert in index order, cut into tiles
+// of 16) and collect its rows into list[0 .. 16).  cnt: E words of scratch LDS.
+// Returns false when tile v does not exist.  Uniform; ends with a barrier.
+__device__ inline bool route_tile16(const int32_t* __restrict__ idx, int M, int E, int v, int* cnt, int* list,
+                                    int* info, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    for (int m = tid; m < M; m += 256) {
+        const int e = idx[m];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    // tiles per expert over contiguous ranges of experts, then the scan
+    const int per = (E + 255) / 256, e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) mine += (cnt[e] + 15) / 16;
+    int total;
+    int t0 = block_scan_256(mine, wsum, &total);
+    if (v >= total) return false;
+    if (v >= t0 && v < t0 + mine) {
+        for (int e = e0; e < e1; ++e) {
+            const int nt = (cnt[e] + 15) / 16;
+            if (v < t0 + nt) {
+                info[0] = e;
+                info[1] = v - t0;
+                info[2] = min(16, cnt[e] - 16 * (v - t0));
+                break;
+            }
+            t0 += nt;
+        }
+    }
+    __syncthreads();
+    const int e = info[0], first = 16 * info[1], last = first + info[2];
+    // ranks of the expert's rows in index order: wave ballots, waves in order
+    int seen = 0;
+    for (int base = 0; base < M && seen < last; base += 256) {
+        const int m = base + tid;
+        const bool hit = m < M && idx[m] == e;
+        const uint64_t mask = __ballot(hit);
+        if (lane == 0) wsum[wave] = __popcll(mask);
+        __syncthreads();
+        int before = seen, add = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            add += wsum[w];
+        }
+        const int rank = before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+        if (hit && rank >= first && rank < last) list[rank - first] = m;
+        seen += add;
+        __syncthreads();
+    }
+    return true;
+}
+
+template <int S, int E, int MODE, bool SELF>
+__global__ void __launch_bounds__(256)
+indexed_decode(IndexedArgs a) {
+    constexpr int BK = 32;
+    constexpr int PB = BK * 256;                      // panel bytes per slice
+    constexpr int XB = 16 * BK * 2;                   // x bytes per slice
+    constexpr int WSLOT = PB + XB;
+    constexpr int L = PB / 1024 + XB / 1024;          // direct loads per slice
+    static_assert(4 * S * WSLOT <= 160 * 1024 - 256 && 4 * S * WSLOT >= 4 * 8 * 64 * 16 &&
+                  4 * S * WSLOT >= kIdxMaxExperts * 4, "LDS ring size");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * S * WSLOT];
+    __shared__ int lrows[16], linfo[4], lsum[8];
+
+    const int tiles_n = (a.N + 127) / 128;
+    const int tv = blockIdx.x / tiles_n, tn = blockIdx.x - tv * tiles_n;
+    const int32_t* list;
+    int expert, rows;
+    if constexpr (SELF) {
+        // the ring is free until the first load below
+        if (!route_tile16(a.idx, a.M, a.E, tv, (int*)smem, lrows, linfo, lsum)) return;
+        list = lrows;
+        expert = linfo[0];
+        rows = linfo[2];
+    } else {
+        if (tv >= a.ws[0]) return;                    // an unused slot (uniform)
+        const int4 tile = ((const int4*)(a.ws + idx_ws_tiles(a.M)))[tv];
+        list = a.ws + kIdxHeaderWords + tile.x;
+        expert = tile.y;
+        rows = tile.z;
+    }
+    const int K = a.K;
+    const int n0 = tn * 128;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned char* ring = smem + wave * S * WSLOT;
+
+    const __amdgpu_buffer_rsrc_t rp = matrix_rsrc(a.w + (int64_t)expert * a.sw, 0, K, a.ldw, a.N);
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, 0, a.M, a.ldx, K);
+
+    // panel load j: k-row 4 j + lane / 16, stored chunk lane % 16
+    uint32_t poff[PB / 1024];
+    int pk[PB / 1024];
+#pragma unroll
+    for (int j = 0; j < PB / 1024; ++j) {
+        const int kr = 4 * j + lane / 16;
+        const int c = (lane % 16) ^ (2 * pair_swz(kr));
+        const int n = n0 + 8 * c;
+        pk[j] = kr;
+        poff[j] = n < a.N ? (uint32_t)(((int64_t)kr * a.ldw + n) * 2) : kOOB;
+    }
+    // x load: row lane / 4, stored chunk lane % 4
+    const int xr = lane / 4;
+    const int xc = (lane % 4) ^ ((xr >> 2) & 3);
+    const int xk = 8 * xc;
+    const uint32_t xoff = xr < rows ? (uint32_t)(((int64_t)list[xr] * a.ldx + xk) * 2) : kOOB;
+    const uint32_t pstep = (uint32_t)(BK * a.ldw * 2);
+    const int nk = (K + BK - 1) / BK;
+    const int mine = nk > wave ? (nk - wave + 3) / 4 : 0;   // this wave's slices
+
+    // i-th slice of this wave: global slice wave + 4 i
+    auto issue = [&](int i) {
+        const int t = wave + 4 * i;
+        unsigned char* slot = ring + (i % S) * WSLOT;
+#pragma unroll
+        for (int j = 0; j < PB / 1024; ++j) {
+            const bool in = i < mine && poff[j] != kOOB && t * BK + pk[j] < K;
+            lds_dma16(rp, slot + j * 1024, in ? poff[j] + (uint32_t)t * pstep : kOOB);
+        }
+        const bool in = i < mine && xoff != kOOB && t * BK + xk < K;
+        lds_dma16(rx, slot + PB, in ? xoff + (uint32_t)t * (BK * 2) : kOOB);
+    };
+
+    // transposing reads: lane (q = lane / 16, s = lane % 16) addresses k-row
+    // 8 q + 4 h + s / 4 and the 8-byte piece at column 16 b + 4 (s % 4); the
+    // row's pair swizzle is pair_swz(8 q + s / 4) for both h
+    const int q = lane >> 4, s = lane & 15;
+    const int psw = pair_swz(8 * q + (s >> 2));
+    const uint32_t abase = (8 * q + (s >> 2)) * 256 + 8 * (s & 1);
+    uint32_t aoff[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) aoff[b] = abase + ((2 * (b ^ psw) + ((s & 3) >> 1)) << 4);
+    // x read (B operand): row s, chunk q
+    const uint32_t boff = PB + s * 64 + ((q ^ ((s >> 2) & 3)) << 4);
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = (f32x4){};
+    for (int i = 0; i < S - 1; ++i) issue(i);
+    for (int i = 0; i < mine; ++i) {
+        // slot (i - 1) % S: this wave's reads of it finished before its MFMAs
+        issue(i + S - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * L) : "memory");
+        const unsigned char* slot = ring + (i % S) * WSLOT;
+        const u32x4 xb = *(const u32x4*)(slot + boff);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint2 lo = lds_read_tr16(slot, aoff[b]);
+            const uint2 hi = lds_read_tr16(slot, aoff[b] + 4 * 256);
+            acc[b] = mfma16x16x32<E>((u32x4){lo.x, lo.y, hi.x, hi.y}, xb, acc[b]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // add the 4 partial tiles in wave order; wave w finishes blocks 2 w, 2 w + 1
+    __syncthreads();
+    f32x4* red = (f32x4*)smem;                        // [wave][block][lane]
+#pragma unroll
+    for (int b = 0; b < 8; ++b) red[(wave * 8 + b) * 64 + lane] = acc[b];
+    __syncthreads();
+    if (s < rows) {
+        const int m = list[s];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int b = 2 * wave + bb;
+            f32x4 v = red[b * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v += red[(w * 8 + b) * 64 + lane];
+            // element r: column n0 + 16 b + 4 (lane / 16) + r, tile row lane % 16
+            const int n = n0 + 16 * b + 4 * q;
+            if (n < a.N) indexed_store4<E, MODE>(a, m, n, v);
+        }
+    }
+}
+
+template <int E>
+static const void* routed_fn(int cfg, int mode) {
+    if (cfg == 0)
+        return mode == kOutF32 ? (const void*)indexed_decode<4, E, kOutF32, false>
+                               : (const void*)indexed_decode<4, E, kOutRound, false>;
+    if (cfg == 2)
+        return mode == kOutF32 ? (const void*)indexed_decode<4, E, kOutF32, true>
+                               : (const void*)indexed_decode<4, E, kOutRound, true>;
+    return mode == kOutF32 ? (const void*)indexed_routed<256, 256, 2, 4, 2, E, kOutF32>
+                           : (const void*)indexed_routed<256, 256, 2, 4, 2, E, kOutRound>;
+}
+
+hipError_t launch_indexed_routed(int elem, int cfg, const IndexedArgs& a, int mode, hipStream_t stream) {
+    const GemmConfig& g = kIdxConfigs[cfg];
+    if (cfg != 2) {
+        hipLaunchKernelGGL(indexed_route, dim3(1), dim3(1024), 0, stream, a.idx, a.M, a.E, g.bm, a.ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const void* fn = elem == kBF16 ? routed_fn<kBF16>(cfg, mode) : routed_fn<kF16>(cfg, mode);
+    IndexedArgs args = a;
+    args.rows_per_tile = g.bm;
+    void* params[] = {&args};
+    const int64_t tiles_n = (a.N + g.bn - 1) / g.bn;
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_n * a.slots)), dim3(g.wm * g.wn * 64), params, 0, stream);
 }
 
 template <int E>

@@ -50,21 +50,50 @@ constexpr int kSkinnyKStep = 32;
 hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream);
 
 // Indexed contraction (x [M, K] against expert tables W [E, K, N], row m against
-// expert idx[m]): one workgroup per (expert, kIdxCols output columns).
+// expert idx[m]).
 struct IndexedArgs {
     const uint16_t* x;      // [M, K], row stride ldx
     const uint16_t* w;      // [E, K, N]: k-row stride ldw, expert stride sw
     const int32_t* idx;     // [M]
     void* y;                // [M, N], row stride ldy (16-bit words or floats)
+    int32_t* ws;            // workspace (routed path): tile count, row list, tile table
     int64_t ldx, ldw, sw, ldy;
     int E, M, N, K;
     int vec_x;              // x rows load as 16-byte fragments
     int vec_store;          // y takes 4-element vector stores
+    int rows_per_tile;      // routed path: x rows per tile (the kernel's BM)
+    int slots;              // routed path: row-tile slots in the grid (>= tiles used)
 };
+
+// Row-scan kernel (any layout): one workgroup per (expert, kIdxCols columns).
 constexpr int kIdxWaves = 4;
 constexpr int kIdxCols = 64;
 constexpr int kIdxCap = 320;   // rows collected per batch
+
+// Routed kernels (16-byte aligned layouts): a one-workgroup routing pass bins
+// the rows by expert into the workspace, then an MFMA kernel runs one
+// workgroup per (row tile of one expert, column tile).
+constexpr int kIdxMaxExperts = 4096;     // experts the routing pass can bin
+constexpr int kIdxMinRows = 16;          // smallest row tile
+constexpr int64_t kIdxHeaderWords = 64;  // workspace: word 0 = tile count
+// Workspace words before the tile table: header, then the M-entry row list.
+__host__ __device__ inline int64_t idx_ws_tiles(int64_t M) { return (kIdxHeaderWords + M + 3) & ~int64_t(3); }
+// Workspace bytes for up to E experts and M rows (any row tile >= kIdxMinRows).
+inline int64_t idx_ws_bytes(int64_t E, int64_t M) {
+    return (idx_ws_tiles(M) + 4 * ((M + kIdxMinRows - 1) / kIdxMinRows + E)) * 4;
+}
+// Routed configurations: 0 decode (16 x 128 tiles, waves split K), 1 prefill
+// (256 x 256 tiles), 2 decode with the routing done by every workgroup itself
+// (no routing pass; for M <= kIdxSelfRouteRows).
+constexpr int kNumIdxConfigs = 3;
+inline constexpr GemmConfig kIdxConfigs[kNumIdxConfigs] = {
+    {16, 128, 1, 4, 4, 32},
+    {256, 256, 2, 4, 2, 64},
+    {16, 128, 1, 4, 4, 32},
+};
+constexpr int kIdxSelfRouteRows = 4096;
 hipError_t launch_indexed(int elem, const IndexedArgs& a, int mode, hipStream_t stream);
+hipError_t launch_indexed_routed(int elem, int cfg, const IndexedArgs& a, int mode, hipStream_t stream);
 
 // The activation tables of element type elem on `device` (3 x kActWords words:
 // SiLU, tanh GeLU, erf GeLU), built on `stream` by the first call and waited for

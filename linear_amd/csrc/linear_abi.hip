@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/linear_amd.h"
 #include "kernels.h"
 
@@ -137,10 +139,10 @@ bool vector_store_ok(const Request& r) {
 }
 
 // Tile choice for the register-staged kernel (unaligned layouts, not tuned): the
-// larger tile when it still gives every CU a tile.
-int choose_gemm_config(int64_t M, int64_t N) {
+// larger tile when it still gives every CU a tile.  Tiles count over all G groups.
+int choose_gemm_config(int64_t M, int64_t N, int64_t G) {
     const lin::GemmConfig& g = lin::kGemmConfigs[0];
-    const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+    const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn) * G;
     return tiles >= kNumCUs ? 0 : 1;
 }
 
@@ -148,6 +150,7 @@ int choose_gemm_config(int64_t M, int64_t N) {
 // 256x256 tile sustains the highest rate, and a partial last wave of large tiles
 // costs little, so: the largest tile that still gives every CU at least one tile;
 // when no tile size does, the one that keeps the most CUs busy at its rate.
+// Tiles count over all G groups of a grouped call.
 struct StreamChoice {
     int cfg;
     double rate;   // sustained throughput relative to the 256x256 tile
@@ -155,13 +158,14 @@ struct StreamChoice {
 // kStreamConfigs in order: 256x256, 256x128, 128x256, 128x128, 64x64
 const StreamChoice kStreamOrder[] = {{0, 1.00}, {1, 0.94}, {2, 0.85}, {3, 0.80}, {4, 0.57}};
 
-int choose_stream_config(int64_t M, int64_t N) {
+int choose_stream_config(int64_t M, int64_t N, int64_t G) {
     int best = 4;
     double best_score = -1.0;
     for (const StreamChoice& c : kStreamOrder) {
         const lin::GemmConfig& g = lin::kStreamConfigs[c.cfg];
-        const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
-        if (tiles > kMaxGridX / 64) continue;
+        const int64_t per_group = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+        if (per_group > kMaxGridX / 64) continue;
+        const int64_t tiles = per_group * G;
         if (tiles >= kNumCUs) return c.cfg;
         const double score = (double)tiles * c.rate;
         if (score > best_score) {
@@ -188,7 +192,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         p->grid = gx * gy * r.G;
     } else {
         const bool stream = p->vector_io != 0;
-        const int c = stream ? choose_stream_config(r.M, r.N) : choose_gemm_config(r.M, r.N);
+        const int c = stream ? choose_stream_config(r.M, r.N, r.G) : choose_gemm_config(r.M, r.N, r.G);
         const lin::GemmConfig& g = stream ? lin::kStreamConfigs[c] : lin::kGemmConfigs[c];
         p->tile_m = g.bm;
         p->tile_n = g.bn;
@@ -287,13 +291,13 @@ int32_t run(const Request& r, void* stream) {
         a.tiles_n = (int)((r.N + 15) / 16);
         e = lin::launch_skinny(r.elem, a, vec, mode, (hipStream_t)stream);
     } else if (vec) {
-        const int c = choose_stream_config(r.M, r.N);
+        const int c = choose_stream_config(r.M, r.N, r.G);
         const lin::GemmConfig& g = lin::kStreamConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
         e = lin::launch_gemm_stream(r.elem, c, a, mode, (hipStream_t)stream);
     } else {
-        const int c = choose_gemm_config(r.M, r.N);
+        const int c = choose_gemm_config(r.M, r.N, r.G);
         const lin::GemmConfig& g = lin::kGemmConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
@@ -306,22 +310,38 @@ int32_t run(const Request& r, void* stream) {
     return LINEAR_OK;
 }
 
-// The indexed contraction: checks, then one launch.
+// The routed indexed kernels need 16-byte chunks of x rows and of table rows,
+// 32-bit byte offsets within x and within one table, and few enough experts
+// for the routing pass.
+bool indexed_routed_ok(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw, int64_t E,
+                       int64_t M, int64_t N, int64_t K) {
+    return E <= lin::kIdxMaxExperts && (uintptr_t)x % 16 == 0 && (uintptr_t)w % 16 == 0 && ldx % 8 == 0 &&
+           ldw % 8 == 0 && sw % 8 == 0 && K % 8 == 0 && N % 8 == 0 &&
+           ((M - 1) * ldx + K) * 2 < (int64_t(1) << 31) && (K * ldw + N) * 2 < (int64_t(1) << 31);
+}
+
+// The indexed contraction: checks, then the launches.
 int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                     int64_t sw, const int32_t* idx, void* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
-                    int64_t K, void* stream) {
+                    int64_t K, void* ws, int64_t ws_bytes, void* stream) {
     if (M < 0 || N < 0 || K < 0 || E < 0) return LINEAR_E_SHAPE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim || E > kMaxGridY) return LINEAR_E_SHAPE;
     if (M == 0 || N == 0 || E == 0) return LINEAR_OK;   // no row has an expert: nothing to write
-    if (!y || !idx) return LINEAR_E_NULL;
+    if (!y || !idx || !ws) return LINEAR_E_NULL;
     if (K > 0 && (!x || !w)) return LINEAR_E_NULL;
     if (ldx < K || ldw < N || ldy < N || sw < K * ldw) return LINEAR_E_STRIDE;
     if (ldx > kMaxLdOut || ldw > kMaxLdOut || ldy > kMaxLdOut) return LINEAR_E_STRIDE;
+    const int64_t need = lin::idx_ws_bytes(E, M);
+    if (ws_bytes < need || (uintptr_t)ws % 16 != 0) return LINEAR_E_WORKSPACE;
     const int64_t eb = f32_out ? 4 : 2;
     const Extent ey = extent(y, M, ldy, N, eb);
+    const Extent ew = extent(ws, 1, need, need, 1);
     if (overlaps(ey, extent(x, M, ldx, K))) return LINEAR_E_ALIAS;
     if (K > 0 && overlaps(ey, extent_g(w, E, sw, K, ldw, N))) return LINEAR_E_ALIAS;
     if (overlaps(ey, extent(idx, 1, M, M, 4))) return LINEAR_E_ALIAS;
+    if (overlaps(ew, ey) || overlaps(ew, extent(x, M, ldx, K)) || overlaps(ew, extent(idx, 1, M, M, 4)) ||
+        (K > 0 && overlaps(ew, extent_g(w, E, sw, K, ldw, N))))
+        return LINEAR_E_ALIAS;
     int dev = 0;
     int32_t st = check_device(&dev);
     if (st != LINEAR_OK) return st;
@@ -330,6 +350,7 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     a.w = w;
     a.idx = idx;
     a.y = y;
+    a.ws = (int32_t*)ws;
     a.ldx = ldx;
     a.ldw = ldw;
     a.sw = sw;
@@ -340,7 +361,21 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     a.K = (int)K;
     a.vec_x = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0) ? 1 : 0;
     a.vec_store = ((uintptr_t)y % (f32_out ? 16 : 8) == 0) && (ldy % 4 == 0) ? 1 : 0;
-    const hipError_t e = lin::launch_indexed(elem, a, f32_out ? lin::kOutF32 : lin::kOutRound, (hipStream_t)stream);
+    a.rows_per_tile = 0;
+    a.slots = 0;
+    const int mode = f32_out ? lin::kOutF32 : lin::kOutRound;
+    hipError_t e;
+    if (indexed_routed_ok(x, ldx, w, ldw, sw, E, M, N, K)) {
+        // rows per expert on average decide the row tile
+        const int cfg = M > 16 * E ? 1 : M <= lin::kIdxSelfRouteRows ? 2 : 0;
+        const lin::GemmConfig& g = lin::kIdxConfigs[cfg];
+        // every expert with rows ends at most one partial tile
+        a.slots = (int)((M + g.bm - 1) / g.bm + std::min(E, M));
+        if ((int64_t)a.slots * ((N + g.bn - 1) / g.bn) > kMaxGridX) return LINEAR_E_SHAPE;
+        e = lin::launch_indexed_routed(elem, cfg, a, mode, (hipStream_t)stream);
+    } else {
+        e = lin::launch_indexed(elem, a, mode, (hipStream_t)stream);
+    }
     if (e != hipSuccess) {
         g_last_hip_error = (int32_t)e;
         return LINEAR_E_LAUNCH;
@@ -352,28 +387,37 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
 
 extern "C" {
 
+int64_t linear_indexed_workspace_bytes(int64_t E, int64_t M) {
+    if (E < 0 || M < 0 || E > kMaxGridY || M > kMaxDim) return -1;
+    return lin::idx_ws_bytes(E, M);
+}
+
 int32_t linear_f16_indexed(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
-                           const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
-                           int64_t K, void* stream) {
-    return run_indexed(lin::kF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+                           const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N, int64_t K,
+                           void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_indexed(lin::kF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, workspace, workspace_bytes,
+                       stream);
 }
 
 int32_t linear_bf16_indexed(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
-                            const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
-                            int64_t K, void* stream) {
-    return run_indexed(lin::kBF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+                            const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N, int64_t K,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_indexed(lin::kBF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, workspace, workspace_bytes,
+                       stream);
 }
 
 int32_t linear_f16_indexed_f32out(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
-                                  const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
-                                  int64_t K, void* stream) {
-    return run_indexed(lin::kF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+                                  const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_indexed(lin::kF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, workspace, workspace_bytes,
+                       stream);
 }
 
 int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
-                                   const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
-                                   int64_t K, void* stream) {
-    return run_indexed(lin::kBF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, stream);
+                                   const int32_t* idx, float* y, int64_t ldy, int64_t E, int64_t M, int64_t N, int64_t K,
+                                   void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_indexed(lin::kBF16, true, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, workspace, workspace_bytes,
+                       stream);
 }
 
 int32_t linear_f16(const uint16_t* x, int64_t ldx, const uint16_t* weight, int64_t ldw,
@@ -501,6 +545,7 @@ const char* linear_status_string(int32_t status) {
         case LINEAR_E_LAUNCH: return "kernel launch failed";
         case LINEAR_E_EPILOGUE: return "invalid epilogue program: step count or step code";
         case LINEAR_E_CAPTURE: return "the first activation epilogue on a device cannot run under stream capture";
+        case LINEAR_E_WORKSPACE: return "workspace not 16-byte aligned or smaller than linear_indexed_workspace_bytes";
         default: return "unknown status";
     }
 }

@@ -1,0 +1,53 @@
+// sched.h -- workgroup-to-tile mapping and instruction-order helpers shared by
+// the MFMA kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace lin {
+
+// Tile (tm, tn) of workgroup bid in a tiles_m x tiles_n grid.  Consecutive
+// workgroup ids are dealt round-robin over the 8 XCDs, so each XCD is given a
+// contiguous run of tiles, walked in groups of 8 tile-rows: tiles running
+// together on one XCD share operand panels in its L2.
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int G = tiles_m * tiles_n;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int q = G >> 3, r = G & 7;
+    const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * GROUP;
+    const int gm = min(tiles_m - first_m, GROUP);
+    const int rem = t - g * per_group;
+    tm = first_m + rem % gm;
+    tn = rem / gm;
+}
+
+// Calls f.template operator()<I>() for I = B .. N-1 (compile-time loop).
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < N) {
+        f.template operator()<B>();
+        static_for<B + 1, N>(f);
+    }
+}
+
+// Instruction order of one K step of the streaming GEMM: its first MFMA, the
+// NREAD fragment reads of the next step, then the other NMFMA - 1 MFMAs with ND
+// loads spaced evenly between them.
+template <int NMFMA, int NREAD, int ND>
+__device__ __forceinline__ void order_step() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NREAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+    constexpr int q = (NMFMA - 1) / (ND + 1);
+    static_for<0, ND>([&]<int d>() {
+        if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x008, q, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    });
+    if constexpr (NMFMA - 1 - q * ND > 0) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - 1 - q * ND, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+}  // namespace lin

@@ -187,11 +187,26 @@ def test_grouped_noops_and_device_check():
 
 
 I = 0x7F6000000000   # fake idx
+WS = 0x7F7000000000  # fake workspace
 
 
-def call_indexed(x=X, ldx=64, w=W, ldw=32, sw=64 * 32, idx=I, y=Y, ldy=32, E=4, M=8, N=32, K=64, f32=False):
+def call_indexed(x=X, ldx=64, w=W, ldw=32, sw=64 * 32, idx=I, y=Y, ldy=32, E=4, M=8, N=32, K=64, f32=False,
+                 ws=WS, ws_bytes=1 << 20):
     fn = la._lib().linear_f16_indexed_f32out if f32 else la._lib().linear_f16_indexed
-    return fn(x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, None)
+    return fn(x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, ws, ws_bytes, None)
+
+
+@needs_lib
+def test_indexed_workspace_bytes():
+    f = la._lib().linear_indexed_workspace_bytes
+    assert f(-1, 4) == -1 and f(4, -1) == -1 and f(65536, 4) == -1
+    # header, row list, then one 16-byte tile record per possible tile
+    for E, M in ((1, 1), (8, 32), (8, 4096), (256, 100), (4096, 1 << 20)):
+        n = f(E, M)
+        assert n % 16 == 0
+        assert n >= 4 * (M + 1) + 16 * ((M + 31) // 32 + E)
+        assert n < 4 * (M + 72) + 16 * ((M + 31) // 32 + E)
+    assert la.indexed_workspace_bytes(8, 32) == f(8, 32)
 
 
 @needs_lib
@@ -208,6 +223,12 @@ def call_indexed(x=X, ldx=64, w=W, ldw=32, sw=64 * 32, idx=I, y=Y, ldy=32, E=4, 
     (dict(ldy=31), la.LINEAR_E_STRIDE),
     (dict(y=W + 3 * 64 * 32 * 2), la.LINEAR_E_ALIAS),   # y inside the last expert table
     (dict(idx=Y + 16), la.LINEAR_E_ALIAS),
+    (dict(ws=0), la.LINEAR_E_NULL),
+    (dict(ws_bytes=0), la.LINEAR_E_WORKSPACE),
+    (dict(ws=WS + 8), la.LINEAR_E_WORKSPACE),           # misaligned
+    (dict(ws=Y), la.LINEAR_E_ALIAS),                    # workspace over y
+    (dict(ws=X + 64), la.LINEAR_E_ALIAS),               # workspace over x
+    (dict(ws=I - 64), la.LINEAR_E_ALIAS),               # workspace over idx
 ])
 def test_indexed_validation(kw, code, f32):
     assert call_indexed(f32=f32, **kw) == code
@@ -215,8 +236,8 @@ def test_indexed_validation(kw, code, f32):
 
 @needs_lib
 def test_indexed_noops_and_device_check():
-    assert call_indexed(E=0, x=0, w=0, idx=0, y=0) == la.LINEAR_OK
-    assert call_indexed(M=0, idx=0) == la.LINEAR_OK
+    assert call_indexed(E=0, x=0, w=0, idx=0, y=0, ws=0) == la.LINEAR_OK
+    assert call_indexed(M=0, idx=0, ws=0) == la.LINEAR_OK
     rc = call_indexed()
     assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
     if not torch.cuda.is_available():

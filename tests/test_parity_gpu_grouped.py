@@ -160,7 +160,12 @@ IDX_CASES = {
 
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 @pytest.mark.parametrize("case", list(IDX_CASES))
-@pytest.mark.parametrize("M,E,N,K", [(13, 5, 19, 29), (40, 4, 64, 256), (700, 3, 130, 72), (32, 8, 200, 520)])
+@pytest.mark.parametrize("M,E,N,K", [
+    (13, 5, 19, 29), (700, 3, 130, 72), (64, 5000, 16, 16),        # row-scan kernel: unaligned, many experts
+    (40, 4, 64, 256), (32, 8, 200, 520), (50, 4096, 24, 24),         # decode tiles, routed in the workgroup
+    (4500, 300, 136, 40),                                            # decode tiles after the routing pass
+    (96, 3, 384, 64), (700, 3, 136, 72), (1100, 2, 264, 520),        # 256-row tiles, ragged N and K
+])
 def test_indexed_integers_bit_exact(orc, M, E, N, K, case, dtype):
     elem = elem_of(dtype)
     r = 30 if dtype == F16 else 6
@@ -225,6 +230,26 @@ def test_indexed_strided_tables_and_unaligned_x(orc, dtype):
     mask = np.ones(g.shape, bool)
     mask[:, 2:2 + N] = False
     assert (g[mask] == words(torch.tensor([3.0], dtype=dtype))[0]).all()
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_indexed_reused_workspace(orc, dtype):
+    """One caller-owned workspace through calls of different sizes and both row
+    tiles: each call rebuilds the binning it needs."""
+    elem = elem_of(dtype)
+    E, N, K = 4, 136, 200
+    ws = torch.empty(la.indexed_workspace_bytes(E, 900), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xAB)
+    for M, seed in ((900, 1), (40, 2), (300, 3), (7, 4)):
+        x, w, idx = workloads.make_indexed_inputs(E, M, N, K, 0.1, seed=seed, dtype=dtype)
+        fn = la.linear_bf16_indexed if dtype == BF else la.linear_f16_indexed
+        y = words(fn(x.to(DEV), w.to(DEV), idx.to(DEV), workspace=ws))
+        y_ref, _ = orc.indexed(x, w, idx.numpy(), elem=elem)
+        _, A = orc.indexed_band(x, w, idx.numpy(), elem=elem)
+        ok, rep = tolerance.check_proj(y, y_ref, A, elem=elem)
+        assert ok.all(), (M, rep)
+    with pytest.raises(ValueError):
+        fn(x.to(DEV), w.to(DEV), idx.to(DEV), workspace=ws[:16])
 
 
 def test_indexed_empty_cases(orc):

@@ -204,8 +204,8 @@ def test_indexed_workspace_bytes():
     for E, M in ((1, 1), (8, 32), (8, 4096), (256, 100), (4096, 1 << 20)):
         n = f(E, M)
         assert n % 16 == 0
-        assert n >= 4 * (M + 1) + 16 * ((M + 31) // 32 + E)
-        assert n < 4 * (M + 72) + 16 * ((M + 31) // 32 + E)
+        assert n >= 4 * (M + 1) + 16 * ((M + 15) // 16 + E)
+        assert n < 4 * (M + 72) + 16 * ((M + 15) // 16 + E)
     assert la.indexed_workspace_bytes(8, 32) == f(8, 32)
 
 

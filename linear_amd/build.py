@@ -29,6 +29,7 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
+    "-Rpass-analysis=kernel-resource-usage",   # per-kernel registers, spills, scratch (checked below)
 ]
 
 
@@ -39,16 +40,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _resources(text: str) -> dict:
+    """Kernel name -> {field: value} from hipcc's kernel-resource-usage remarks."""
+    res, name = {}, None
+    for line in text.splitlines():
+        if "[-Rpass-analysis=kernel-resource-usage]" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+        key, _, val = body.partition(": ")
+        if key == "Function Name":
+            name = val
+            res[name] = {}
+        elif name is not None:
+            res[name][key] = val
+    return res
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    out = r.stdout + r.stderr
+    noise = ("is not a recognized feature for this target", "kernel-resource-usage")
+    msg = "\n".join(l for l in out.splitlines()
+                    if not any(n in l for n in noise) and not l.lstrip().startswith(("|", "^", "In file included from"))
+                    and not (l[:6].strip().isdigit() and " | " in l))
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, msg))
     if msg.strip():
         print(msg, file=sys.stderr)
+    # every kernel must run from registers and LDS: scratch memory (spills, or an
+    # argument copy indexed at run time) costs a memory round trip per access
+    res = _resources(out)
+    bad = {k: v for k, v in res.items()
+           if v.get("ScratchSize [bytes/lane]", "0") != "0" or v.get("VGPRs Spill", "0") != "0"}
+    with open(os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+        for k, v in sorted(res.items()):
+            f.write("%s %s\n" % (k, " ".join("%s=%s" % (a.replace(" ", "_"), b) for a, b in v.items())))
+    if bad:
+        raise RuntimeError("kernels in %s use scratch memory: %s" % (src, ", ".join(sorted(bad))))
     return obj
 
 

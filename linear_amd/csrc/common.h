@@ -28,9 +28,12 @@ struct EpiArgs {
     const uint16_t* act;    // this element type's tables: SiLU, tanh GeLU, erf GeLU (3 x kActWords)
     int64_t ldr, ldm;
     int nsteps;
-    uint8_t ops[kEpiMaxSteps];
+    uint64_t ops;           // step s in byte s (packed: a kernel indexes no array of its arguments,
+                            // which would move a modified argument copy to scratch memory)
     int vec16;              // bits: 1 y, 2 bias, 4 res, 8 mul allow 16-byte (8-word) accesses
 };
+
+__host__ __device__ inline int epi_op(const EpiArgs& ep, int s) { return (int)((ep.ops >> (8 * s)) & 0xff); }
 
 // Arguments of one linear-layer launch.  Pointers are device pointers to 16-bit
 // words (binary16 or bfloat16, per the kernel's element type); y holds 16-bit
@@ -168,7 +171,7 @@ __device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 template <int E>
 __device__ inline uint16_t epi_apply(const EpiArgs& ep, uint16_t t, int m, int n) {
     for (int s = 0; s < ep.nsteps; ++s) {
-        const int op = ep.ops[s];
+        const int op = epi_op(ep, s);
         if (op == kEpiBias) t = narrow<E>(widen<E>(t) + widen<E>(ep.bias[n]));
         else if (op == kEpiResidual) t = narrow<E>(widen<E>(t) + widen<E>(ep.res[(int64_t)m * ep.ldr + n]));
         else if (op == kEpiMul) t = narrow<E>(widen<E>(t) * widen<E>(ep.mul[(int64_t)m * ep.ldm + n]));
@@ -235,9 +238,9 @@ __device__ inline Extras4 epi_prefetch4(const LinearArgs& a, int m, int nb) {
     const EpiArgs& ep = a.epi;
     bool ub = false, ur = false, uu = false;
     for (int s = 0; s < ep.nsteps; ++s) {
-        ub |= ep.ops[s] == kEpiBias;
-        ur |= ep.ops[s] == kEpiResidual;
-        uu |= ep.ops[s] == kEpiMul;
+        ub |= epi_op(ep, s) == kEpiBias;
+        ur |= epi_op(ep, s) == kEpiResidual;
+        uu |= epi_op(ep, s) == kEpiMul;
     }
     Extras4 x;
 #pragma unroll
@@ -255,7 +258,7 @@ __device__ inline Extras4 epi_prefetch4(const LinearArgs& a, int m, int nb) {
 template <int E>
 __device__ inline void epi_apply4(const EpiArgs& ep, uint16_t t[4], const Extras4& x) {
     for (int s = 0; s < ep.nsteps; ++s) {
-        const int op = ep.ops[s];
+        const int op = epi_op(ep, s);
         if (op >= kEpiSilu) {
             const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
 #pragma unroll

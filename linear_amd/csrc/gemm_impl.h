@@ -186,7 +186,7 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
             for (int k = 0; k < CH; ++k) t[k] = binop8<E, false>(t[k], v[k]);
         }
         for (int s = 0; MODE == kOutEpi && s < ep.nsteps; ++s) {
-            const int op = ep.ops[s];
+            const int op = epi_op(ep, s);
             if (op >= kEpiSilu) {
                 const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
 #pragma unroll

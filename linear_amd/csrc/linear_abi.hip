@@ -271,7 +271,7 @@ int32_t run(const Request& r, void* stream) {
         a.epi.nsteps = ep->nsteps;
         a.epi.vec16 = (al16(r.y, r.ldy) ? 1 : 0) | (al16(ep->bias, 8) ? 2 : 0) |
                       (al16(ep->residual, ep->ldr) ? 4 : 0) | (al16(ep->mul, ep->ldm) ? 8 : 0);
-        for (int s = 0; s < ep->nsteps; ++s) a.epi.ops[s] = (uint8_t)ep->op[s];
+        for (int s = 0; s < ep->nsteps; ++s) a.epi.ops |= (uint64_t)(uint8_t)ep->op[s] << (8 * s);
         if (epi_uses(ep, LINEAR_EPI_SILU) || epi_uses(ep, LINEAR_EPI_GELU_TANH) || epi_uses(ep, LINEAR_EPI_GELU_ERF)) {
             hipError_t te = lin::act_tables(r.elem, dev, (hipStream_t)stream, &a.epi.act);
             if (te == hipErrorStreamCaptureUnsupported) {

@@ -198,6 +198,29 @@ __device__ inline u32x4 binop8(u32x4 x, u32x4 y) {
     return r;
 }
 
+// The activation-table window that the GEMM epilogue copies into LDS: for each
+// sign, the 8192 consecutive words from exponent field kActWinExp<E> on, i.e.
+// |x| in [2^-7, 2) for binary16 and [2^-40, 2^24) for bfloat16, 32 KB in all.
+// Entry (x >> 15) * 8192 + (x & 0x7fff) - (kActWinExp << mantissa bits) holds
+// the table's word for x; other words are read from the table in global memory.
+constexpr int kActWinWords = 16384;
+template <int E> constexpr int kActWinExp = E == kF16 ? 8 : 87;
+template <int E> constexpr uint32_t kActWinBase = (uint32_t)kActWinExp<E> << (E == kF16 ? 10 : 7);
+
+template <int E>
+__device__ inline uint32_t lookup_win(const uint16_t* win, const uint16_t* tab, uint32_t x) {
+    const uint32_t d = (x & 0x7fffu) - kActWinBase<E>;
+    return d < 8192u ? (uint32_t)win[((x >> 15) << 13) | d] : (uint32_t)tab[x];
+}
+
+template <int E>
+__device__ inline u32x4 lookup8_win(const uint16_t* win, const uint16_t* tab, u32x4 x) {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = lookup_win<E>(win, tab, x[q] & 0xffffu) | (lookup_win<E>(win, tab, x[q] >> 16) << 16);
+    return r;
+}
+
 __device__ inline u32x4 lookup8(const uint16_t* tab, u32x4 x) {
     u32x4 r;
 #pragma unroll

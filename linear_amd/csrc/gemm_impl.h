@@ -161,8 +161,11 @@ gemm_kernel(LinearArgs a) {
 // consecutive columns of one row each) and runs the program step by step over
 // up to 8 of them at a time: each step issues every load it needs before using
 // any, and the extra inputs and y move as 16-byte row accesses where aligned.
+// win: the LDS copy of activation step win_op's table window (or none when
+// win_op is 0); other activation steps read their tables from global memory.
 template <int BM, int BN, int NT, int E, int MODE>
-__device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, int m0, int n0, int tid) {
+__device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, int m0, int n0, int tid,
+                                const uint16_t* win = nullptr, int win_op = 0) {
     constexpr int CPR = BN / 8;
     constexpr int CHT = BM * CPR / NT;               // chunks per thread
     constexpr int CH = CHT < 8 ? CHT : 8;            // chunks per pass (bounds register use)
@@ -189,8 +192,13 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
             const int op = epi_op(ep, s);
             if (op >= kEpiSilu) {
                 const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
+                if (op == win_op) {
 #pragma unroll
-                for (int k = 0; k < CH; ++k) t[k] = lookup8(tab, t[k]);
+                    for (int k = 0; k < CH; ++k) t[k] = lookup8_win<E>(win, tab, t[k]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < CH; ++k) t[k] = lookup8(tab, t[k]);
+                }
                 continue;
             }
             u32x4 v[CH];
@@ -264,7 +272,13 @@ gemm_stream(LinearArgs a) {
     static_assert(BN % RPL == 0, "weight rows must fill whole direct loads");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(STAGES >= 2 && STAGES * SLICE <= 160 * 1024, "LDS ring too large");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
+    // after the main loop the ring holds the rounded tile (BM x BN words) and, for
+    // an epilogue program, the LDS window of its first activation's table behind it
+    constexpr int TILEB = BM * BN * 2;
+    constexpr int LDSB = MODE == kOutEpi && TILEB + 2 * kActWinWords > STAGES * SLICE ? TILEB + 2 * kActWinWords
+                                                                                      : STAGES * SLICE;
+    static_assert(LDSB <= 160 * 1024, "LDS too large");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDSB];
 
     int tm, tn;
     tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -462,6 +476,26 @@ gemm_stream(LinearArgs a) {
         static_assert(BM * BN * 2 <= STAGES * SLICE, "the rounded tile must fit in the ring");
         constexpr int CPR = BN / 8;
         __syncthreads();
+        // an epilogue program's first activation: its table window goes into LDS
+        // behind the tile (32 direct loads of 1 KB: for each sign 8192 words from
+        // kActWinBase on), landing while the tile is staged
+        int win_op = 0;
+        if constexpr (MODE == kOutEpi) {
+            for (int s = 0; s < a.epi.nsteps; ++s)
+                if (win_op == 0 && epi_op(a.epi, s) >= kEpiSilu) win_op = epi_op(a.epi, s);
+            if (win_op != 0) {
+                const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(a.epi.act + (win_op - kEpiSilu) * kActWords), (short)0, kActWords * 2, kRsrcWord3);
+                constexpr int PW = 32 / NW;
+                static_assert(32 % NW == 0, "window loads must divide evenly over the waves");
+#pragma unroll
+                for (int q = 0; q < PW; ++q) {
+                    const int j = wave * PW + q, h = j >> 4, piece = j & 15;
+                    const uint32_t word = ((uint32_t)h << 15) + kActWinBase<E> + (uint32_t)piece * 512u;
+                    lds_dma16(rt, smem + TILEB + j * 1024, word * 2u + 16u * (uint32_t)lane);
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -477,8 +511,9 @@ gemm_stream(LinearArgs a) {
                     *(uint2*)(smem + (ml * CPR + (c8 ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
                 }
             }
+        if constexpr (MODE == kOutEpi) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x);
+        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x, (const uint16_t*)(smem + TILEB), win_op);
         return;
     }
 

@@ -702,7 +702,6 @@ hipError_t launch_indexed_routed(int elem, int cfg, const IndexedArgs& a, int mo
     }
     const void* fn = elem == kBF16 ? routed_fn<kBF16>(cfg, mode) : routed_fn<kF16>(cfg, mode);
     IndexedArgs args = a;
-    args.rows_per_tile = g.bm;
     void* params[] = {&args};
     const int64_t tiles_n = (a.N + g.bn - 1) / g.bn;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_n * a.slots)), dim3(g.wm * g.wn * 64), params, 0, stream);

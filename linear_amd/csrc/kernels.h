@@ -61,7 +61,6 @@ struct IndexedArgs {
     int E, M, N, K;
     int vec_x;              // x rows load as 16-byte fragments
     int vec_store;          // y takes 4-element vector stores
-    int rows_per_tile;      // routed path: x rows per tile (the kernel's BM)
     int slots;              // routed path: row-tile slots in the grid (>= tiles used)
 };
 

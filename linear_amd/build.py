@@ -84,6 +84,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
+    # a failed build must not leave the previous library behind for tests and
+    # benchmarks to load
+    if os.path.exists(OUT):
+        os.remove(OUT)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()

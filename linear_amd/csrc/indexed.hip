@@ -258,12 +258,12 @@ __device__ inline uint2 lds_read_tr16(const unsigned char* base, uint32_t off) {
 }
 
 // Swizzle of the panel rows: the 32-byte column pair u of k-row kr sits at pair
-// u ^ pair_swz(kr).  The LDS serves a 64-lane 8-byte read 32 lanes at a time;
-// the 32 lanes of a transposing read address 32-byte pieces in the k-rows
-// kb + (0 .. 3) or kb + 8 + (0 .. 3) (kb a multiple of 16) and in two adjacent
-// pairs (32 x 32 fragments) or one pair of rows kb + (0 .. 3) and kb + 8 + (0 .. 3)
-// (16 x 16 fragments).  pair_swz takes 2 (kr % 4) + (kr / 8) % 2, so those eight
-// pieces land on eight different 32-byte bank groups either way: no conflicts.
+// u ^ pair_swz(kr).  The LDS serves a 64-lane 8-byte read 32 lanes at a time, and
+// those 32 lanes of a transposing read fetch eight 32-byte pieces: the four
+// k-rows 4i .. 4i + 3 in two adjacent pairs (32 x 32 fragments), or those four
+// rows and the four rows 8 further on in one pair (16 x 16 fragments), with
+// 4i mod 16 equal to 0 or 4.  pair_swz(kr) = 2 (kr mod 4) + (kr / 8) mod 2 sends
+// the eight pieces to eight different 32-byte bank groups: no conflicts.
 __host__ __device__ constexpr int pair_swz(int kr) { return 2 * (kr & 3) | ((kr >> 3) & 1); }
 
 // Workgroup (tile v, column tile tn): y[rows of v, n0 .. n0 + BN) for tile v's
@@ -344,9 +344,9 @@ indexed_routed(IndexedArgs a) {
 
     const int wn = wave % WN, wm = wave / WN;
     // transposing reads: lane (q = lane / 16, s = lane % 16) addresses k-row
-    // kq + s / 4 + (4h + 16 ks) and the 8-byte piece at column
-    // nb + 16 (q % 2) + 4 (s % 4) of its fragment; the piece's pair swizzle
-    // depends only on s / 4 and q / 2
+    // kq + 4 h + 16 ks with kq = 8 (q / 2) + s / 4, and the 8-byte piece at column
+    // nb + 16 (q % 2) + 4 (s % 4) of its fragment; the row's pair swizzle is
+    // pair_swz(kq) for every h and ks
     const int q = lane >> 4, s = lane & 15;
     const int kq = 8 * (q >> 1) + (s >> 2);
     const int sw = pair_swz(kq);
@@ -468,18 +468,6 @@ indexed_routed(IndexedArgs a) {
     }
 }
 
-// Decode-shaped tiles (at most 16 rows): the contraction is the streaming of the
-// panel.  Workgroup (tile v, 128 columns); its 4 waves split K, wave w taking
-// the 32-k slices t = w, w + 4, ...: each streams its slices of the panel (32
-// k-rows x 256 bytes, 8 direct loads of four whole 256-byte row pieces) and of
-// the tile's x rows (16 rows x 64 bytes, 1 direct load) through a private ring
-// of S slots and waits only for its own loads, so the loop has no barrier.
-// v_mfma_f32_16x16x32: panel columns as A (two transposing reads per 16
-// columns), x rows as B.  At the end the 4 partial tiles are added in wave
-// order through LDS.
-//
-// Panel slot: k-row kr, 32-byte column pair u at pair u ^ pair_swz(kr).
-// x slot: row r (64 bytes), 16-byte chunk c at chunk c ^ ((r >> 2) & 3).
 // Exclusive prefix sum of v over the 256 threads; *total gets the sum.  Uses
 // wsum (8 words) and ends with a barrier.
 __device__ inline int block_scan_256(int v, int* wsum, int* total) {
@@ -557,6 +545,20 @@ __device__ inline bool route_tile16(const int32_t* __restrict__ idx, int M, int 
     return true;
 }
 
+// Decode-shaped tiles (at most 16 rows): the contraction is the streaming of the
+// panel.  Workgroup (tile v, 128 columns); its 4 waves split K, wave w taking
+// the 32-k slices t = w, w + 4, ...: each streams its slices of the panel (32
+// k-rows x 256 bytes, 8 direct loads of four whole 256-byte row pieces) and of
+// the tile's x rows (16 rows x 64 bytes, 1 direct load) through a private ring
+// of S slots and waits only for its own loads, so the loop has no barrier.
+// SELF: the workgroup finds its tile itself (route_tile16) instead of reading
+// the routing pass's table.
+// v_mfma_f32_16x16x32: panel columns as A (two transposing reads per 16
+// columns), x rows as B.  At the end the 4 partial tiles are added in wave
+// order through LDS.
+//
+// Panel slot: k-row kr, 32-byte column pair u at pair u ^ pair_swz(kr).
+// x slot: row r (64 bytes), 16-byte chunk c at chunk c ^ ((r >> 2) & 3).
 template <int S, int E, int MODE, bool SELF>
 __global__ void __launch_bounds__(256)
 indexed_decode(IndexedArgs a) {

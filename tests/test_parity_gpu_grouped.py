@@ -155,6 +155,7 @@ IDX_CASES = {
     "some_unused": lambda M, E, g: torch.randint(0, max(1, E // 2), (M,), generator=g) * 2,
     "invalid_rows": lambda M, E, g: torch.where(torch.rand(M, generator=g) < 0.3,
                                                 torch.tensor(E + 5), torch.randint(-1, E, (M,), generator=g)),
+    "no_expert": lambda M, E, g: torch.full((M,), -1),      # every workgroup finds no tile
 }
 
 
@@ -165,6 +166,7 @@ IDX_CASES = {
     (40, 4, 64, 256), (32, 8, 200, 520), (50, 4096, 24, 24),         # decode tiles, routed in the workgroup
     (4500, 300, 136, 40),                                            # decode tiles after the routing pass
     (96, 3, 384, 64), (700, 3, 136, 72), (1100, 2, 264, 520),        # 256-row tiles, ragged N and K
+    (33, 1, 64, 64), (600, 1, 128, 128),                             # a single expert
 ])
 def test_indexed_integers_bit_exact(orc, M, E, N, K, case, dtype):
     elem = elem_of(dtype)

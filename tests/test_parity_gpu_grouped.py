@@ -138,6 +138,16 @@ def test_grouped_workload_sampled(orc, dtype):
     y1, y2 = fn(xd, wd, bd), fn(xd, wd, bd)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # every GEMM tile feeds each output the same k order, so a group equals the
+    # plain call on its slices even where the two pick different tiles (here
+    # 256 x 256 for the grouped call against 64 x 64 for one group alone)
+    plain = la.linear_bf16 if dtype == BF else la.linear_f16
+    plan_g = la.linear_f16_plan(xd[0], wd[:wl.N], bd[:wl.N])
+    assert (plan_g["tile_m"], plan_g["tile_n"]) == (64, 64)
+    for g in (0, wl.G - 1):
+        yp = plain(xd[g], wd[g * wl.N:(g + 1) * wl.N], bd[g * wl.N:(g + 1) * wl.N])
+        torch.cuda.synchronize()
+        assert torch.equal(yp.view(torch.int16), y1[g].view(torch.int16)), g
     yw = words(y1)
     for g in (0, wl.G // 2, wl.G - 1):
         ms, ns = workloads.sample_points(wl.M, wl.N, 2048, seed=g)

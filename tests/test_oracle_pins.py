@@ -1,4 +1,6 @@
 """The CPU oracle against its pins (no GPU)."""
+import concurrent.futures
+
 import numpy as np
 import pytest
 
@@ -14,17 +16,23 @@ def test_toy_shapes_match_pages():
     pins.pin_toy_shapes()
 
 
+def _all_binary32_words(check):
+    """Run check(words) over all 2^32 binary32 words in chunks of 2^24, on 8
+    threads (the oracle's ctypes calls and torch's conversions release the GIL)."""
+    chunk = 1 << 24
+
+    def one(start):
+        check(np.arange(chunk, dtype=np.uint32) + np.uint32(start))
+
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        list(ex.map(one, range(0, 1 << 32, chunk)))
+
+
 def test_rne_exhaustive_all_binary32_words(orc):
     """binary32 -> binary16 RNE for all 2^32 words against torch's conversion."""
-    chunk = 1 << 26
-    for start in range(0, 1 << 32, chunk):
-        words = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
-        pins.check_rne_words(orc, words)
+    _all_binary32_words(lambda words: pins.check_rne_words(orc, words))
 
 
 def test_bf16_rne_exhaustive_all_binary32_words(orc):
     """binary32 -> bfloat16 RNE for all 2^32 words against torch's conversion."""
-    chunk = 1 << 26
-    for start in range(0, 1 << 32, chunk):
-        words = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
-        pins.check_bf16_rne_words(orc, words)
+    _all_binary32_words(lambda words: pins.check_bf16_rne_words(orc, words))

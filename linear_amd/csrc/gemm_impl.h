@@ -2,29 +2,22 @@
 //
 // Computes the projection tile C[n, m] = sum_k weight[n, k] * x[m, k] with
 // v_mfma_f32_32x32x16_f16 / _bf16 (exact products, FP32 accumulation), then the
-// contract's epilogue in registers: round to the element type, and with a bias
-// widen, add b[n] in FP32 and round again ("tensor programs, part 1", section "One
-// Program and One Numerical Contract"; the Inductor capture's cast sequence; for
-// bfloat16, "The Graph IR", op table, ContractionEpilogue: a BF16 head rounds to
-// BF16 before the first epilogue step).  The FP32-output mode stores the sums
-// unrounded (the op table's DenseContraction produces f32).
+// contract's epilogue: round to the element type, and with a bias widen, add b[n]
+// in FP32 and round again ("tensor programs, part 1", section "One Program and One
+// Numerical Contract"; the Inductor capture's cast sequence; for bfloat16, "The
+// Graph IR", op table, ContractionEpilogue: a BF16 head rounds to BF16 before the
+// first epilogue step), or an epilogue program of several such steps.  The
+// FP32-output mode stores the sums unrounded (the op table's DenseContraction
+// produces f32).
 //
-// Layout choices:
+// Layout choices (both kernels):
 //  - The weight tile is the MFMA A operand and the x tile the B operand, so the
-//    accumulator rows are output columns n: each lane ends up holding four
-//    consecutive n of one output row m and stores them as one 8-byte write.
+//    accumulator rows are output columns n: each lane holds four consecutive n of
+//    one output row m.
 //  - Both operands are K-contiguous in HBM and are read in place ([N, K] weight,
-//    no transpose copy, as the op table's dense contraction requires):
-//    each thread moves 16-byte chunks along K; a wave covers 8 full 128-byte
-//    rows per load instruction.
-//  - K-slices of BK = 64 are staged through LDS, double buffered: the loads of
-//    slice t+1 are issued before the MFMAs of slice t, written to the other LDS
-//    buffer after them, one barrier per slice.
-//  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ ((r >> 1) & 7).  The LDS serves a 16-byte-per-lane read 16 lanes (256
-//    bytes) at a time, so the 16 consecutive rows one such group reads at one K
-//    offset must fall in 16 different 16-byte bank groups: two rows share each
-//    256-byte span and the XOR separates the rest.
+//    no transpose copy, as the op table's dense contraction requires).
+//  - Every tile feeds each output the same sequence of 16-wide k chunks into one
+//    accumulator, so the tile choice never changes a result.
 //  - Ragged M, N and K need no special tiles: loads go through buffer
 //    resources whose range ends at the matrix's last valid element, so rows past
 //    M or N and K chunks past K read as zero; stores are masked.
@@ -32,6 +25,8 @@
 //    round-robin over the 8 XCDs) owns a contiguous run of tiles, walked in
 //    groups of 8 tile-rows, so tiles running together share x and weight panels
 //    in that XCD's L2.
+// The streaming kernel (aligned layouts) and the register-staged one (any
+// layout) are described where they are defined below.
 #pragma once
 
 #include "common.h"
@@ -43,8 +38,14 @@ namespace lin {
 
 // Register-staged variant for layouts the streaming kernel cannot take (K, ldx or
 // ldw not a multiple of 8, or x / weight not 16-byte aligned): every element is
-// loaded with its own masked 2-byte buffer load, staged through registers into the
-// double-buffered LDS tiles.
+// loaded with its own masked 2-byte buffer load, staged through registers into
+// double-buffered LDS tiles (the loads of slice t + 1 are issued before the MFMAs
+// of slice t and written to the other buffer after them; one barrier per slice).
+// LDS rows are 128 bytes, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7): the
+// LDS serves a 16-byte-per-lane read 16 lanes (256 bytes) at a time, and the 16
+// consecutive rows such a group reads at one K offset then fall in 16 different
+// 16-byte bank groups.  The epilogue runs in registers: each lane finishes its
+// four consecutive columns of one row and stores them with one 8-byte write.
 template <int BM, int BN, int WM, int WN, int E, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(LinearArgs a) {

@@ -12,7 +12,8 @@
  * projection rounded to FP16 before the bias addition, output FP16), and the
  * Inductor capture's epilogue (both operands widened to f32, added, rounded to
  * f16).  The weight is contracted in its stored [N, K] order with no transposed or
- * widened copy, as the poot Graph IR op table describes a dense contraction.
+ * widened copy, as "The Graph IR" op table describes a dense contraction
+ * (DenseContraction).
  *
  * Conventions shared by every entry point
  * ---------------------------------------

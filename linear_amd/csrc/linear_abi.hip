@@ -2,8 +2,9 @@
 //
 // All shape, stride, alias and path checks run on the host before anything is
 // enqueued, and kernel choice is a host decision made from the static shapes
-// (as the poot Graph IR pages do it: shapes are inferred on the host and GEMV
-// versus GEMM is chosen when the call is planned, not inside a kernel).
+// ("The Graph IR", section "Host-side shape inference", and the op table's MatMul
+// row: shapes are known on the host and GEMV versus GEMM is chosen when the call
+// is planned, not inside a kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>

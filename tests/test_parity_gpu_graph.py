@@ -111,3 +111,64 @@ def test_indexed_graph_replays(E, M, N, K):
         return (la.linear_f16_indexed(x, w, idx, out=torch.zeros(M, N, dtype=F16, device=DEV)),)
 
     replay_check(lambda: la.linear_f16_indexed(x, w, idx, out=y, workspace=ws), refill, lambda: (y,), eager)
+
+
+def test_indexed_calls_on_two_streams_with_their_own_workspaces():
+    """Two indexed calls in flight at once on two streams, each with its workspace,
+    equal the same calls made one after the other."""
+    E, M, N, K = 8, 600, 256, 512
+    xa, w, ia = workloads.make_indexed_inputs(E, M, N, K, 0.05, seed=21)
+    xb, _, ib = workloads.make_indexed_inputs(E, M, N, K, 0.05, seed=22)
+    xa, xb, w, ia, ib = (t.to(DEV) for t in (xa, xb, w, ia, ib))
+    ref_a = la.linear_f16_indexed(xa, w, ia)
+    ref_b = la.linear_f16_indexed(xb, w, ib)
+    torch.cuda.synchronize()
+    wsa = torch.empty(la.indexed_workspace_bytes(E, M), dtype=torch.uint8, device=DEV)
+    wsb = torch.empty_like(wsa)
+    ya = torch.empty(M, N, dtype=F16, device=DEV)
+    yb = torch.empty(M, N, dtype=F16, device=DEV)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(4):
+        la.linear_f16_indexed(xa, w, ia, out=ya, stream=sa, workspace=wsa)
+        la.linear_f16_indexed(xb, w, ib, out=yb, stream=sb, workspace=wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), ref_a.view(torch.int16))
+    assert torch.equal(yb.view(torch.int16), ref_b.view(torch.int16))
+
+
+CAPTURE_FIRST_ACTIVATION = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import linear_amd as la
+x = torch.randn(64, 64, device="cuda").half()
+w = torch.randn(64, 64, device="cuda").half()
+y = torch.zeros(64, 64, device="cuda").half()
+s = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+code = None
+with torch.cuda.graph(g, stream=s):
+    try:
+        la.linear_f16_epilogue(x, w, [la.EPI_SILU], out=y)
+    except la.LinearError as e:
+        code = e.code
+torch.cuda.synchronize()
+print("capture status", code)
+la.linear_f16_epilogue(x, w, [la.EPI_SILU], out=y)   # eager: builds the tables
+torch.cuda.synchronize()
+print("eager ok")
+"""
+
+
+def test_first_activation_under_capture_is_refused():
+    """The first activation call on a device builds its tables and waits for
+    them, which stream capture cannot hold: it returns LINEAR_E_CAPTURE and
+    enqueues nothing; the same call made eagerly afterwards works."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", CAPTURE_FIRST_ACTIVATION, root], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "capture status %d" % la.LINEAR_E_CAPTURE in r.stdout, r.stdout
+    assert "eager ok" in r.stdout

@@ -11,10 +11,14 @@ call.  Inputs are synthetic, seeded, resident in HBM before timing starts.
 
 The line also carries, under "prefill", the MFMA-bound shapes (toy 1024x1024x768,
 attention projection 8192x4096x4096, MLP up-projection 4096x14336x4096, ragged
-down-projection 2000x4000x14336) in TFLOP/s against the FP16 dense MFMA peak,
+down-projection 2000x4000x14336) in TFLOP/s against the FP16 dense MFMA peak;
+under "variants", the bfloat16, FP32-output and epilogue-program forms, the
+grouped contraction (8 x 512x4096x4096) and the indexed contraction
+(moe_decode: 32 rows over 8 experts of [4096, 4096]; moe_prefill: 4096 rows);
 and, under "cpu_baseline", the CPU oracle timed on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-variants] [--no-cpu]
+       python bench.py --only <workload> [--variant V]   (one workload alone, for profiling)
 """
 from __future__ import annotations
 

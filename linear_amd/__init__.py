@@ -1,6 +1,8 @@
 """MI355X (gfx950) FP16 linear layer: y = FP16(FP16(x @ weight.T) + b).
 
-A thin ctypes binding over the C ABI of ``liblinear_amd.so`` (declared in
+Also its bfloat16 form, the unrounded FP32 sums, multi-step epilogue programs,
+and the grouped and indexed (per-row expert) contractions.  A thin ctypes
+binding over the C ABI of ``liblinear_amd.so`` (declared in
 ``include/linear_amd.h``).  The functions carry the C entry points' names and
 only marshal arguments: every step of the computation runs in the library's
 HIP kernels.  PyTorch supplies device memory and the stream.  If the library

@@ -83,7 +83,8 @@ inline int64_t idx_ws_bytes(int64_t E, int64_t M) {
 }
 // Routed configurations: 0 decode (16 x 128 tiles, waves split K), 1 prefill
 // (256 x 256 tiles), 2 decode with the routing done by every workgroup itself
-// (no routing pass; for M <= kIdxSelfRouteRows).
+// (no routing pass; for M <= kIdxSelfRouteRows and a grid at most two
+// workgroups deep per CU, since every workgroup repeats the routing).
 constexpr int kNumIdxConfigs = 3;
 inline constexpr GemmConfig kIdxConfigs[kNumIdxConfigs] = {
     {16, 128, 1, 4, 4, 32},

@@ -366,12 +366,16 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     const int mode = f32_out ? lin::kOutF32 : lin::kOutRound;
     hipError_t e;
     if (indexed_routed_ok(x, ldx, w, ldw, sw, E, M, N, K)) {
-        // rows per expert on average decide the row tile
-        const int cfg = M > 16 * E ? 1 : M <= lin::kIdxSelfRouteRows ? 2 : 0;
-        const lin::GemmConfig& g = lin::kIdxConfigs[cfg];
+        // rows per expert on average decide the row tile; decode tiles route
+        // themselves (no routing pass) when every workgroup's routing, which all
+        // of them repeat, runs at most two workgroups deep per CU
+        int cfg = M > 16 * E ? 1 : 0;
+        const lin::GemmConfig& g0 = lin::kIdxConfigs[cfg];
         // every expert with rows ends at most one partial tile
-        a.slots = (int)((M + g.bm - 1) / g.bm + std::min(E, M));
-        if ((int64_t)a.slots * ((N + g.bn - 1) / g.bn) > kMaxGridX) return LINEAR_E_SHAPE;
+        a.slots = (int)((M + g0.bm - 1) / g0.bm + std::min(E, M));
+        const int64_t grid = (int64_t)a.slots * ((N + g0.bn - 1) / g0.bn);
+        if (grid > kMaxGridX) return LINEAR_E_SHAPE;
+        if (cfg == 0 && M <= lin::kIdxSelfRouteRows && grid <= 2 * kNumCUs) cfg = 2;
         e = lin::launch_indexed_routed(elem, cfg, a, mode, (hipStream_t)stream);
     } else {
         e = lin::launch_indexed(elem, a, mode, (hipStream_t)stream);

@@ -6,8 +6,8 @@
   bit against the oracle (long K loops, 32-bit buffer offsets near 2^21 bytes
   per row).
 - M = 65536 rows (256 GEMM row tiles through the XCD remap).
-- Indexed calls with 64 and 256 experts (the 256-row kernel after the routing
-  pass; the decode kernel routing in the workgroup).
+- Indexed calls with 64 and 256 experts (the 256-row kernel and the 16-row
+  kernel, both after the routing pass).
 """
 import numpy as np
 import pytest
@@ -73,7 +73,7 @@ def test_many_row_tiles_sampled(orc):
 
 
 @pytest.mark.parametrize("E,M,N,K", [(64, 8192, 512, 1024), (256, 2048, 256, 512)],
-                         ids=["64_experts_routed", "256_experts_self_routed"])
+                         ids=["64_experts_256_row_tiles", "256_experts_16_row_tiles"])
 def test_many_experts_sampled(orc, E, M, N, K):
     x, w, idx = workloads.make_indexed_inputs(E, M, N, K, 1.0 / 32, seed=E)
     y = words(la.linear_f16_indexed(x.to(DEV), w.to(DEV), idx.to(DEV)))

@@ -176,6 +176,7 @@ IDX_CASES = {
     (40, 4, 64, 256), (32, 8, 200, 520), (50, 4096, 24, 24),         # decode tiles, routed in the workgroup
     (4500, 300, 136, 40),                                            # decode tiles after the routing pass
     (96, 3, 384, 64), (700, 3, 136, 72), (1100, 2, 264, 520),        # 256-row tiles, ragged N and K
+    (200, 2, 200, 64), (1300, 3, 520, 136),                          # 256-row tiles: short last tiles
     (33, 1, 64, 64), (600, 1, 128, 128),                             # a single expert
 ])
 def test_indexed_integers_bit_exact(orc, M, E, N, K, case, dtype):

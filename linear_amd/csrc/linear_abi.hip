@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/linear_amd.h"
 #include "kernels.h"
@@ -208,7 +209,7 @@ int32_t plan(const Request& r, linear_plan* p) {
 
 // Device check, cached per device: the current device must be a gfx950.
 int32_t check_device(int* dev_out) {
-    static int cached[64];  // 0 unknown, 1 gfx950, 2 other
+    static std::atomic<int> cached[64];  // 0 unknown, 1 gfx950, 2 other (callers may be on several threads)
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0) {

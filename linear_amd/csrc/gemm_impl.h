@@ -23,7 +23,7 @@
 //    M or N and K chunks past K read as zero; stores are masked.
 //  - Workgroup ids are remapped so that each XCD (consecutive ids are dealt
 //    round-robin over the 8 XCDs) owns a contiguous run of tiles, walked in
-//    groups of 8 tile-rows, so tiles running together share x and weight panels
+//    groups of 4 tile-rows, so tiles running together share x and weight panels
 //    in that XCD's L2.
 // The streaming kernel (aligned layouts) and the register-staged one (any
 // layout) are described where they are defined below.

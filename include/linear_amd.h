@@ -310,7 +310,11 @@ int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx,
                                    int64_t E, int64_t M, int64_t N, int64_t K,
                                    void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Which kernel a call would launch.  Pure host function: touches no device. */
+/* Which kernels a call would launch.  Pure host function: touches no device.
+ * A GEMM call whose largest tiles would leave a last wave of workgroups at most
+ * half full over the GPU's CUs is split by output columns into two launches of
+ * the same kernel family: columns [0, split_n) in whole waves of the first tile,
+ * columns [split_n, N) with the tile chosen for that part alone. */
 typedef struct linear_plan {
     int32_t path;       /* LINEAR_PATH_GEMM or LINEAR_PATH_SKINNY */
     int32_t tile_m;     /* output rows (m) per workgroup */
@@ -318,7 +322,11 @@ typedef struct linear_plan {
     int32_t tile_k;     /* K elements per main-loop stage (GEMM) or per wave step (skinny) */
     int32_t threads;    /* threads per workgroup */
     int32_t vector_io;  /* 1: 16-byte loads; 0: element-wise loader */
-    int64_t grid;       /* workgroups launched */
+    int64_t grid;       /* workgroups launched (the first launch when split) */
+    int64_t split_n;    /* 0: one launch; else the first column of the second launch */
+    int32_t tile_m2;    /* the second launch's tile (0 when not split) */
+    int32_t tile_n2;
+    int64_t grid2;      /* the second launch's workgroups (0 when not split) */
 } linear_plan;
 
 /*

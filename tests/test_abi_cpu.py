@@ -265,6 +265,24 @@ def test_plans_for_the_workloads():
 
 
 @needs_lib
+def test_column_split_rule():
+    """A GEMM call whose 256 x 256 tiles leave a last wave at most half full over
+    256 CUs is split by columns: whole waves first, the rest with its own tile."""
+    p = plan(4096, 14336, 4096)                      # mlp_up: 896 tiles, 3.5 waves
+    assert (p["tile_m"], p["tile_n"], p["grid"]) == (256, 256, 768)
+    assert (p["split_n"], p["tile_m2"], p["tile_n2"], p["grid2"]) == (12288, 256, 128, 256)
+    p = plan(4096, 4352, 512)                       # 272 tiles: the last 256 columns alone
+    assert (p["grid"], p["split_n"], p["tile_m2"], p["tile_n2"], p["grid2"]) == (256, 4096, 64, 64, 256)
+    p = plan(300, 34800, 72)                        # 2 x 136 tiles, ragged remainder
+    assert (p["grid"], p["split_n"], p["tile_m2"], p["tile_n2"], p["grid2"]) == (256, 32768, 64, 64, 160)
+    for M, N in [(8192, 4096), (2000, 4000), (4096, 27 * 256), (1024, 1024), (4096, 16128)]:
+        # whole waves, a last wave more than half full, or another tile: one launch
+        p = plan(M, N, 512)
+        assert p["split_n"] == 0 and p["grid2"] == 0 and p["tile_m2"] == 0, (M, N, p)
+    assert plan(4096, 14336, 4096, path=la.PATH_SKINNY)["split_n"] == 0
+
+
+@needs_lib
 def test_plan_falls_back_to_elementwise_loader():
     assert plan(64, 64, 63)["vector_io"] == 0          # K % 8 != 0
     assert plan(64, 64, 64, x=X + 2)["vector_io"] == 0  # misaligned x

@@ -71,6 +71,19 @@ def test_small_integers_bit_exact(orc, path, M, N, K):
     full_check(orc, x, w, b, path, exact=True)
 
 
+# Shapes whose 256 x 256 tiles leave a last wave at most half full: the call runs
+# as two launches split by output columns (the second with 64 x 64 tiles here).
+SPLIT_SHAPES = [(200, 66000, 64), (300, 34800, 72)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_column_split_bit_exact(orc, M, N, K):
+    x, w, b = workloads.small_integers(M, N, K, seed=M + N)
+    p = la.linear_f16_plan(x, w, b)
+    assert p["split_n"] > 0 and p["grid2"] > 0, p
+    full_check(orc, x, w, b, la.PATH_GEMM, exact=True)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_integer_ties_and_overflow_bit_exact(orc, path):
     """Sums that are odd integers in (2048, 4096), 2 mod 4 in (4096, 8192), and past

@@ -197,6 +197,24 @@ def test_programs_on_integer_data_bit_exact(orc, prog, path, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_program_through_a_column_split_bit_exact(orc, dtype):
+    """A shape that runs as two launches split by columns: the second launch reads
+    bias, residual and gate at the shifted columns and writes its own."""
+    elem = elem_of(dtype)
+    M, N, K = 300, 34800, 72
+    prog = [la.EPI_BIAS, la.EPI_GELU_ERF, la.EPI_RESIDUAL, la.EPI_MUL]
+    x, w, b = workloads.small_integers(M, N, K, seed=93, dtype=dtype)
+    r, u = extras(M, N, dtype, 94, ints=True)
+    assert la.linear_f16_plan(x, w, b)["split_n"] > 0
+    y = words(epi(dtype, x, w, prog, bias=b, residual=r, mul=u, path=la.PATH_GEMM))
+    _, p_ref = orc.linear(x, w, None, elem=elem)
+    bb = np.broadcast_to(words(b)[None, :], (M, N))
+    want = orc.epilogue(prog, p_ref, bias=bb, res=words(r), mul=words(u), elem=elem)
+    ok = eq_words(y, want, elem)
+    assert ok.all(), (~ok).sum()
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_k0_program_of_the_empty_sum(orc, path, dtype):
     elem = elem_of(dtype)

@@ -47,7 +47,8 @@ def replay_check(call, refill, outs, eager, replays=3):
 
 
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (1, 1024, 768), (300, 520, 264), (1024, 1024, 768)])
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (1, 1024, 768), (300, 520, 264), (1024, 1024, 768),
+                                   (300, 34800, 72)])   # the last one runs as two launches split by columns
 def test_linear_graph_replays(M, N, K, dtype):
     x, w, b = (t.to(DEV) for t in workloads.make_inputs(M, N, K, 1.0 / np.sqrt(K), seed=M, dtype=dtype))
     fn = la.linear_bf16 if dtype == BF else la.linear_f16

@@ -327,6 +327,16 @@ def test_f16_sums_small_integers_bit_exact(orc, path, M, N, K):
     full_check(orc, x, w, b, path, F16, exact=True)
 
 
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_column_split_with_sums_bit_exact(orc, dtype):
+    """A shape that runs as two launches split by columns, in both element types:
+    bias, bias-less and FP32-output calls bit for bit on integer data."""
+    M, N, K = 300, 34800, 72
+    x, w, b = workloads.small_integers(M, N, K, seed=95, dtype=dtype)
+    assert la.linear_f16_plan(x.view(torch.float16), w.view(torch.float16))["split_n"] > 0
+    full_check(orc, x, w, b, la.PATH_GEMM, dtype, exact=True)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (7, 1000, 520), (257, 129, 72), (512, 384, 1024),
                                    (130, 70, 333)])

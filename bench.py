@@ -15,7 +15,8 @@ down-projection 2000x4000x14336) in TFLOP/s against the FP16 dense MFMA peak;
 under "variants", the bfloat16, FP32-output and epilogue-program forms, the
 grouped contraction (8 x 512x4096x4096) and the indexed contraction
 (moe_decode: 32 rows over 8 experts of [4096, 4096]; moe_prefill: 4096 rows);
-and, under "cpu_baseline", the CPU oracle timed on this host.
+under "cpu_baseline", the CPU oracle timed on this host; and, under "context",
+the per-launch floor of the smallest call and one decode call timed alone.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-variants] [--no-cpu]
        python bench.py --only <workload> [--variant V]   (one workload alone, for profiling)
@@ -213,6 +214,41 @@ def bench_decode(args, torch, la, workloads, stream, dtype=None):
         "plan_m1": la.linear_f16_plan(x1, wbase, b),
     }
     return ms, detail
+
+
+def bench_context(torch, la, workloads, stream):
+    """Context for the decode figures, not part of `value`: the per-launch floor of
+    the smallest call (1 x 16 x 32, one workgroup) replayed in a graph, and one
+    decode call (M = 1) timed alone between two events.  Every tensor a graph or a
+    call uses stays referenced here until its last replay has finished."""
+    log("context: launch floor (1 x 16 x 32 in a graph)")
+    x = torch.ones((1, 32), dtype=torch.float16, device="cuda")
+    w = torch.ones((16, 32), dtype=torch.float16, device="cuda")
+    b = torch.zeros((16,), dtype=torch.float16, device="cuda")
+    y = torch.empty((1, 16), dtype=torch.float16, device="cuda")
+    g = capture(lambda i: la.linear_f16(x, w, b, out=y, stream=stream), 64, stream, torch)
+    g.replay()
+    floor = sorted(time_region(g, 20, stream, torch) / (20 * 64) for _ in range(5))[2] * 1e3
+    torch.cuda.synchronize()
+    del g
+
+    log("context: single gemv1 calls")
+    x1, w1, b1 = workloads.workload_inputs("gemv1", seed=0, device="cuda")
+    y1 = torch.empty((1, w1.shape[0]), dtype=torch.float16, device="cuda")
+    singles = []
+    for _ in range(60):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            la.linear_f16(x1, w1, b1, out=y1, stream=stream)
+            end.record(stream)
+        end.synchronize()
+        singles.append(start.elapsed_time(end) * 1e3)
+    singles = sorted(singles[10:])
+    return {"launch_floor_us": round(floor, 3),
+            "single_call_gemv1_us": {"median": round(singles[len(singles) // 2], 3), "min": round(singles[0], 3)}}
 
 
 # epilogue programs timed by the bench: name -> (steps, reads a residual, reads a gate input)
@@ -417,6 +453,8 @@ def main():
             dt = torch.bfloat16 if args.variant == "bf16" else torch.float16
             ms, _ = bench_decode(args, torch, la, workloads, stream, dt)
             log("decode ms/step %.5f" % ms)
+        elif args.only == "context":
+            log(json.dumps(bench_context(torch, la, workloads, stream)))
         elif args.only in workloads.GROUPED:
             log(json.dumps(bench_grouped(args.only, torch, la, workloads, stream, 40, args.variant)))
         elif args.only in workloads.INDEXED:
@@ -434,6 +472,8 @@ def main():
     per_launch_s = ms * 1e-3 / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
     log("decode: %.3f us/step, %.1f GB/s" % (ms * 1e3, value))
+    context = bench_context(torch, la, workloads, stream)
+    log("context", json.dumps(context))
 
     prefill = {}
     if not args.no_prefill:
@@ -502,6 +542,7 @@ def main():
             "us_per_launch": round(per_launch_s * 1e6, 3),
         },
         "cpu_baseline": cpu,
+        "context": context,
         "prefill": prefill,
         "variants": variants,
     }

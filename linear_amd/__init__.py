@@ -161,11 +161,31 @@ def _mat(t: torch.Tensor, name: str, dtype=torch.float16):
 
 
 def _stream_handle(stream, *tensors):
-    if stream is not None:
-        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    """The stream a launch goes to, after checking its tensor arguments: every one
+    must be a GPU ('cuda') tensor on the current device, where the library
+    launches (a host address handed to a kernel would fault the GPU, so it is
+    refused here instead).  stream: a torch stream, a raw handle or None (the
+    current stream of that device)."""
+    dev = None
     for t in tensors:
-        if t is not None and t.is_cuda:
-            return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("every tensor argument must be on the GPU (a 'cuda' device); got one on %s" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensor arguments on two devices: %s and %s" % (dev, t.device))
+    if dev is not None and dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError("the tensors are on %s but the current device is cuda:%d (the library launches on the "
+                         "current device; call under torch.cuda.device(%s))" % (dev, torch.cuda.current_device(), dev))
+    if stream is not None:
+        sdev = getattr(stream, "device", None)
+        if sdev is not None and dev is not None and torch.device(sdev) != dev:
+            raise ValueError("the stream belongs to %s but the tensors are on %s" % (sdev, dev))
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if dev is not None:
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     return ctypes.c_void_p(0)
 
 
@@ -196,7 +216,7 @@ def linear_f16(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor, out: torc
     if b is None:
         raise ValueError("linear_f16 needs a bias; use linear_f16_nobias")
     xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out)
-    rc = _lib().linear_f16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    rc = _lib().linear_f16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, weight, b, out))
     _check(rc, "linear_f16")
     return out
 
@@ -205,7 +225,7 @@ def linear_f16_nobias(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor |
                       stream=None) -> torch.Tensor:
     """proj = FP16(x @ weight.T) on the GPU."""
     xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out)
-    rc = _lib().linear_f16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    rc = _lib().linear_f16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, weight, out))
     _check(rc, "linear_f16_nobias")
     return out
 
@@ -215,7 +235,7 @@ def linear_f16_ex(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None,
     """linear_f16 with a forced path (PATH_AUTO / PATH_GEMM / PATH_SKINNY) and optional bias."""
     xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out)
     rc = _lib().linear_f16_ex(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, int(path),
-                              _stream_handle(stream, x, out))
+                              _stream_handle(stream, x, weight, b, out))
     _check(rc, "linear_f16_ex")
     return out
 
@@ -224,7 +244,8 @@ def linear_f16_f32out(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor |
                       path: int = PATH_AUTO, stream=None) -> torch.Tensor:
     """The unrounded FP32 sums x @ weight.T (float16 operands, float32 output)."""
     xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.float16, torch.float32)
-    rc = _lib().linear_f16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    rc = _lib().linear_f16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path),
+                                  _stream_handle(stream, x, weight, out))
     _check(rc, "linear_f16_f32out")
     return out
 
@@ -235,7 +256,7 @@ def linear_bf16(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor, out: tor
     if b is None:
         raise ValueError("linear_bf16 needs a bias; use linear_bf16_nobias")
     xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out, torch.bfloat16)
-    rc = _lib().linear_bf16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    rc = _lib().linear_bf16(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, _stream_handle(stream, x, weight, b, out))
     _check(rc, "linear_bf16")
     return out
 
@@ -244,7 +265,7 @@ def linear_bf16_nobias(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor 
                        stream=None) -> torch.Tensor:
     """proj = BF16(x @ weight.T)."""
     xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.bfloat16)
-    rc = _lib().linear_bf16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, out))
+    rc = _lib().linear_bf16_nobias(xp, ldx, wp, ldw, yp, ldy, M, N, K, _stream_handle(stream, x, weight, out))
     _check(rc, "linear_bf16_nobias")
     return out
 
@@ -253,7 +274,8 @@ def linear_bf16_ex(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None
                    out: torch.Tensor | None = None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
     """linear_bf16 with a forced path and optional bias."""
     xp, ldx, wp, ldw, bp, out, yp, ldy, M, N, K = _prepare(x, weight, b, out, torch.bfloat16)
-    rc = _lib().linear_bf16_ex(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    rc = _lib().linear_bf16_ex(xp, ldx, wp, ldw, bp, yp, ldy, M, N, K, int(path),
+                               _stream_handle(stream, x, weight, b, out))
     _check(rc, "linear_bf16_ex")
     return out
 
@@ -262,7 +284,8 @@ def linear_bf16_f32out(x: torch.Tensor, weight: torch.Tensor, out: torch.Tensor 
                        path: int = PATH_AUTO, stream=None) -> torch.Tensor:
     """The unrounded FP32 sums x @ weight.T (bfloat16 operands, float32 output)."""
     xp, ldx, wp, ldw, _, out, yp, ldy, M, N, K = _prepare(x, weight, None, out, torch.bfloat16, torch.float32)
-    rc = _lib().linear_bf16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path), _stream_handle(stream, x, out))
+    rc = _lib().linear_bf16_f32out(xp, ldx, wp, ldw, yp, ldy, M, N, K, int(path),
+                                   _stream_handle(stream, x, weight, out))
     _check(rc, "linear_bf16_f32out")
     return out
 
@@ -289,7 +312,7 @@ def _epilogue_call(fn_name, dtype, x, weight, ops, bias, residual, mul, out, pat
         setattr(ep, name, tp)
         setattr(ep, "ldr" if name == "residual" else "ldm", ld)
     rc = getattr(_lib(), fn_name)(xp, ldx, wp, ldw, ctypes.byref(ep), yp, ldy, M, N, K, int(path),
-                                  _stream_handle(stream, x, out))
+                                  _stream_handle(stream, x, weight, bias, residual, mul, out))
     _check(rc, fn_name)
     return out
 
@@ -342,11 +365,11 @@ def _grouped_call(dtype, x, weight, b, out, f32, path, stream):
     if f32:
         name = "linear_%s_grouped_f32out" % tag
         rc = getattr(_lib(), name)(x.data_ptr(), ldx, sx, weight.data_ptr(), ldw, out.data_ptr(), ldy, sy, G, M, N,
-                                   K, int(path), _stream_handle(stream, x, out))
+                                   K, int(path), _stream_handle(stream, x, weight, out))
     else:
         name = "linear_%s_grouped" % tag
         rc = getattr(_lib(), name)(x.data_ptr(), ldx, sx, weight.data_ptr(), ldw, bp, out.data_ptr(), ldy, sy, G, M,
-                                   N, K, int(path), _stream_handle(stream, x, out))
+                                   N, K, int(path), _stream_handle(stream, x, weight, b, out))
     _check(rc, name)
     return out
 
@@ -407,7 +430,8 @@ def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
     tag = "bf16" if dtype == torch.bfloat16 else "f16"
     name = "linear_%s_indexed%s" % (tag, "_f32out" if f32 else "")
     rc = getattr(_lib(), name)(xp, ldx, w.data_ptr(), ldw, sw, idx.data_ptr(), yp, ldy, E, M, N, K,
-                               workspace.data_ptr(), workspace.numel(), _stream_handle(stream, x, out))
+                               workspace.data_ptr(), workspace.numel(),
+                               _stream_handle(stream, x, w, idx, out, workspace))
     _check(rc, name)
     return out
 

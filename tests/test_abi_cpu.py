@@ -265,6 +265,31 @@ def test_plans_for_the_workloads():
 
 
 @needs_lib
+def test_binding_refuses_host_tensors():
+    """A host tensor handed to a kernel would fault the GPU: every entry point of
+    the binding refuses it with ValueError before the library is called."""
+    f16, bf = torch.float16, torch.bfloat16
+    x, w, b = torch.zeros(4, 8, dtype=f16), torch.zeros(6, 8, dtype=f16), torch.zeros(6, dtype=f16)
+    xb, wb, bb = x.to(bf), w.to(bf), b.to(bf)
+    idx = torch.zeros(4, dtype=torch.int32)
+    calls = [
+        (la.linear_f16, (x, w, b)), (la.linear_f16_nobias, (x, w)), (la.linear_f16_ex, (x, w, b)),
+        (la.linear_f16_f32out, (x, w)), (la.linear_bf16, (xb, wb, bb)), (la.linear_bf16_nobias, (xb, wb)),
+        (la.linear_bf16_ex, (xb, wb, None)), (la.linear_bf16_f32out, (xb, wb)),
+        (la.linear_f16_epilogue, (x, w, [la.EPI_BIAS], b)), (la.linear_bf16_epilogue, (xb, wb, [la.EPI_SILU])),
+        (la.linear_f16_grouped, (x.view(1, 4, 8), w, b)), (la.linear_bf16_grouped, (xb.view(1, 4, 8), wb)),
+        (la.linear_f16_grouped_f32out, (x.view(1, 4, 8), w)), (la.linear_bf16_grouped_f32out, (xb.view(1, 4, 8), wb)),
+        (la.linear_f16_indexed, (x, w.view(1, 8, 6), idx)), (la.linear_bf16_indexed, (xb, wb.view(1, 8, 6), idx)),
+        (la.linear_f16_indexed_f32out, (x, w.view(1, 8, 6), idx)),
+        (la.linear_bf16_indexed_f32out, (xb, wb.view(1, 8, 6), idx)),
+        (la.linear, (x, w, b)),
+    ]
+    for fn, args in calls:
+        with pytest.raises(ValueError, match="on the GPU"):
+            fn(*args)
+
+
+@needs_lib
 def test_column_split_rule():
     """A GEMM call whose 256 x 256 tiles leave a last wave at most half full over
     256 CUs is split by columns: whole waves first, the rest with its own tile."""

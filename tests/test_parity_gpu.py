@@ -294,6 +294,11 @@ def test_paths_agree_on_exact_data(orc):
 def test_argument_errors_raise(orc):
     x = torch.zeros(4, 8, dtype=torch.float16, device=DEV)
     w = torch.zeros(6, 8, dtype=torch.float16, device=DEV)
+    # one host tensor among device tensors is refused before any launch
+    with pytest.raises(ValueError, match="on the GPU"):
+        la.linear_f16(x, w, torch.zeros(6, dtype=torch.float16))
+    with pytest.raises(ValueError, match="on the GPU"):
+        la.linear_f16_nobias(x, w, out=torch.empty(4, 6, dtype=torch.float16))
     with pytest.raises(la.LinearArgumentError):
         la.linear_f16_ex(x, w, None, out=x[:, :6].contiguous().view(4, 6)[:, :6], path=7)
     with pytest.raises(ValueError):

@@ -26,7 +26,10 @@
  *    neither allocates, frees nor keeps them after the call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream)
  *    and the call returns without synchronising.  Results are visible after the
- *    stream is synchronised.
+ *    stream is synchronised.  A call enqueues kernel launches only (one, or two:
+ *    a column split of a large GEMM, see linear_plan, and the indexed call's
+ *    routing pass), no allocation, copy or memset, so it can be captured into a
+ *    HIP graph (the first activation call on a device excepted, see below).
  *  - Only y[m, n] for m < M, n < N is written; stride padding is never touched.
  *  - Rounding is IEEE round-to-nearest-even with subnormals kept (no flush to
  *    zero) and overflow to infinity; the empty sum (K == 0) is +0.

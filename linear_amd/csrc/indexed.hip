@@ -448,23 +448,69 @@ indexed_routed(IndexedArgs a) {
     }
 #undef LIN_IDX_ISSUE
 
-    // accumulator (i, j) element 4 b + r: panel column nb + 8 b + 4 (lane / 32) + r,
-    // tile row wm * TM + 32 j + lane % 32
+    // The tile goes out in row order through the freed ring, as in the dense
+    // kernel: each lane stages its accumulators (element 4 b + r of (i, j) is tile
+    // column wn TN + 32 i + 8 b + 4 (lane / 32) + r of tile row wm TM + 32 j +
+    // lane % 32) with 16-byte chunk c of a staged row at c ^ (row mod chunks per
+    // row), then every thread stores whole 16-byte chunks of the gathered rows.
+    // FP32 sums, twice the bytes of the ring, go out in two bands of rows.
+    {
+        constexpr int NT = NW * 64;
+        constexpr int EB = MODE == kOutF32 ? 4 : 2;            // output bytes per element
+        constexpr int EPC = 16 / EB;                          // elements per chunk
+        constexpr int CPR = BN / EPC;                         // chunks per tile row
+        constexpr int PASSES = (BM * BN * EB + STAGES * SLICE - 1) / (STAGES * SLICE);
+        constexpr int RPP = BM / PASSES;                      // tile rows per band
+        constexpr int CHT = RPP * CPR / NT;                   // chunks per thread and band
+        static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
+        static_assert((RPP * CPR) % NT == 0, "chunks must divide evenly over the threads");
+        const bool vec = a.vec_store && ((uintptr_t)a.y % 16 == 0) && (a.ldy % EPC == 0);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int tr = wm * TM + j * 32 + lr;
-        if (tr >= rows) continue;
-        const int m = list[tr];
+        for (int pass = 0; pass < PASSES; ++pass) {
+            __syncthreads();                                  // the ring, or the last band, is free
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+            for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int n = n0 + wn * TN + i * 32 + 8 * b + 4 * lh;
-                if (n < a.N)
-                    indexed_store4<E, MODE>(a, m, n,
-                                            (f32x4){acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
-                                                    acc[i][j][4 * b + 3]});
+                for (int b = 0; b < 4; ++b) {
+                    const int nl = wn * TN + i * 32 + 8 * b + 4 * lh;
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
+                        if (ml < 0 || ml >= RPP) continue;
+                        const f32x4 v = (f32x4){acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
+                                                acc[i][j][4 * b + 3]};
+                        if constexpr (MODE == kOutF32) {
+                            *(f32x4*)(smem + (ml * CPR + ((nl / 4) ^ (ml % CPR))) * 16) = v;
+                        } else {
+                            uint2 u;
+                            u.x = (uint32_t)narrow<E>(v[0]) | ((uint32_t)narrow<E>(v[1]) << 16);
+                            u.y = (uint32_t)narrow<E>(v[2]) | ((uint32_t)narrow<E>(v[3]) << 16);
+                            *(uint2*)(smem + (ml * CPR + ((nl / 8) ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
+                        }
+                    }
+                }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < CHT; ++k) {
+                const int c = (int)threadIdx.x + k * NT, r = c / CPR, cc = c % CPR;
+                const int tr = pass * RPP + r, n = n0 + cc * EPC;
+                if (tr >= rows || n >= a.N) continue;
+                const u32x4 v = *(const u32x4*)(smem + (r * CPR + (cc ^ (r % CPR))) * 16);
+                const int64_t m = list[tr];
+                unsigned char* dst = (unsigned char*)a.y + (m * a.ldy + n) * EB;
+                if (vec && n + EPC <= a.N) {
+                    *(u32x4*)dst = v;
+                } else if constexpr (MODE == kOutF32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) ((uint32_t*)dst)[e] = v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < a.N) ((uint16_t*)dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
             }
+        }
     }
 }
 

@@ -520,11 +520,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 (fp32 accumulate)",
+        "dtype": "f16",
         "data": "synthetic (seeded: x~N(0,1), weight,b~U(-1/64,1/64))",
         "config": {
             "workload": "decode GEMV batch: y=FP16(FP16(x@W.T)+b), x [1,4096] and [16,4096], "
                         "W [4096,4096], b [4096], fp16",
+            "accumulate": "f32 (products exact, FP32 sums rounded once to f16 before the bias)",
             "calls_per_step": launches,
             "weight_copies_rotated": detail["weight_copies"],
             "kernel": "skinny_stream<8, f16, bias> (16 output columns x 16 rows per workgroup, 8 waves, "

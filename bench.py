@@ -510,7 +510,7 @@ def main():
         log(json.dumps(cpu))
 
     line = {
-        "metric": "HBM GB/s and % peak (M<=16 decode GEMV batch); TFLOP/s and % FP16 MFMA peak (large M)",
+        "metric": "TFLOP/s and % FP16 MFMA peak (large M); HBM GB/s and % peak (M≤16)",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

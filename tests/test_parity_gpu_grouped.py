@@ -246,6 +246,45 @@ def test_indexed_strided_tables_and_unaligned_x(orc, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("f32", [False, True], ids=["rounded", "sums"])
+@pytest.mark.parametrize("M,E,N,K", [(600, 3, 264, 72), (40, 4, 136, 64)], ids=["rows256", "rows16"])
+def test_indexed_routed_misaligned_output_with_guard_band(orc, M, E, N, K, f32, dtype):
+    """Aligned x and tables (the routed kernels) with y starting one element into
+    a guard band and an odd row stride: the element-wise stores of the row-order
+    epilogue, bit for bit on integer data; the band and rows without an expert
+    keep their contents."""
+    elem = elem_of(dtype)
+    r = 30 if dtype == F16 else 6
+    x, w = ints((M, K), r, M + K, dtype), ints((E, K, N), r, E + N, dtype)
+    g = torch.Generator().manual_seed(M + 7)
+    idx = torch.where(torch.rand(M, generator=g) < 0.1, torch.tensor(-1), torch.randint(0, E, (M,), generator=g))
+    idx = idx.to(torch.int32)
+    out_dtype = torch.float32 if f32 else dtype
+    guard = torch.full((M, N + 13), 3.0, dtype=out_dtype, device=DEV)
+    yv = guard[:, 1:1 + N]
+    indexed(dtype, x, w, idx, f32=f32, out=yv)
+    y_ref, s_ref = orc.indexed(x, w, idx.numpy(), elem=elem)
+    valid = (idx.numpy() >= 0) & (idx.numpy() < E)
+    gh = guard.cpu()
+    if f32:
+        got = gh[:, 1:1 + N].numpy()
+        assert np.array_equal(got[valid].view(np.uint32), s_ref[valid].view(np.uint32))
+        assert (got[~valid] == 3.0).all()
+        band = np.ones(gh.shape, bool)
+        band[:, 1:1 + N] = False
+        assert (gh.numpy()[band] == 3.0).all()
+    else:
+        gw = words(gh)
+        ok = eq_words(gw[:, 1:1 + N][valid], y_ref[valid], elem)
+        assert ok.all(), (~ok).sum()
+        three = words(torch.tensor([3.0], dtype=dtype))[0]
+        assert (gw[:, 1:1 + N][~valid] == three).all()
+        band = np.ones(gw.shape, bool)
+        band[:, 1:1 + N] = False
+        assert (gw[band] == three).all()
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 def test_indexed_reused_workspace(orc, dtype):
     """One caller-owned workspace through calls of different sizes and both row
     tiles: each call rebuilds the binning it needs."""

@@ -457,7 +457,9 @@ def linear_bf16_indexed_f32out(x, w, idx, out=None, stream=None, workspace=None)
 
 def linear_f16_plan(x: torch.Tensor, weight: torch.Tensor, b: torch.Tensor | None = None,
                     out: torch.Tensor | None = None, path: int = PATH_AUTO) -> dict:
-    """The kernel and tile a call would use (host only)."""
+    """The kernel and tile a call would use (host only): path, tile_m/tile_n/tile_k,
+    threads, vector_io, grid; for a GEMM split by columns into two launches also
+    split_n (the second launch's first column), tile_m2/tile_n2 and grid2."""
     if out is None:
         out = torch.empty((x.shape[0], weight.shape[0]), dtype=torch.float16, device="meta")
         yp, ldy = 0x100000000, max(weight.shape[0], 1)

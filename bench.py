@@ -147,6 +147,12 @@ def rotation_sets(bytes_per_set: int) -> int:
     return max(2, math.ceil(ROTATE_BYTES / max(bytes_per_set, 1)))
 
 
+def graph_calls(sets: int, minimum: int = 64) -> int:
+    """Calls per captured graph: a multiple of the input sets (each used equally)
+    and at least `minimum`, since every replay adds a graph launch of its own."""
+    return sets * max(1, math.ceil(minimum / sets))
+
+
 def capture(fn, calls, stream, torch):
     """Capture fn(0) .. fn(calls-1) into one HIP graph on `stream` (launch overhead of
     Python and ctypes stays out of the timed region; the kernels allocate nothing
@@ -309,11 +315,12 @@ def bench_gemm(name, torch, la, workloads, stream, calls, variant="f16"):
         else:
             fn(xs[k], ws[k], b, out=ys[k], stream=stream)
 
-    graph = capture(call, sets, stream, torch)
-    replays = max(1, calls // sets)
+    per_graph = graph_calls(sets)
+    graph = capture(call, per_graph, stream, torch)
+    replays = max(1, calls // per_graph)
     graph.replay()
     times = [time_region(graph, replays, stream, torch) for _ in range(5)]
-    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    ms = sorted(times)[len(times) // 2] / (replays * per_graph)
     del graph
     tflops = wl.flops / (ms * 1e-3) / 1e12
     plan = la.linear_f16_plan(x, w, b)
@@ -345,11 +352,12 @@ def bench_grouped(name, torch, la, workloads, stream, calls, dtype_name="f16"):
         k = i % sets
         fn(xs[k], ws[k], b, out=ys[k], stream=stream)
 
-    graph = capture(call, sets, stream, torch)
-    replays = max(1, calls // sets)
+    per_graph = graph_calls(sets)
+    graph = capture(call, per_graph, stream, torch)
+    replays = max(1, calls // per_graph)
     graph.replay()
     times = [time_region(graph, replays, stream, torch) for _ in range(5)]
-    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    ms = sorted(times)[len(times) // 2] / (replays * per_graph)
     del graph, xs, ws, ys
     return {"G": wl.G, "M": wl.M, "N": wl.N, "K": wl.K, "variant": dtype_name,
             "us_per_call": round(ms * 1e3, 3), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 1),
@@ -375,11 +383,12 @@ def bench_indexed(name, torch, la, workloads, stream, calls, dtype_name="f16"):
         k = i % sets
         fn(x, ws[k], idx, out=ys[k], stream=stream, workspace=work)
 
-    graph = capture(call, sets, stream, torch)
-    replays = max(1, calls // sets)
+    per_graph = graph_calls(sets)
+    graph = capture(call, per_graph, stream, torch)
+    replays = max(1, calls // per_graph)
     graph.replay()
     times = [time_region(graph, replays, stream, torch) for _ in range(5)]
-    ms = sorted(times)[len(times) // 2] / (replays * sets)
+    ms = sorted(times)[len(times) // 2] / (replays * per_graph)
     del graph, ws, ys
     return {"E": wl.E, "M": wl.M, "N": wl.N, "K": wl.K, "experts_used": used, "variant": dtype_name,
             "us_per_call": round(ms * 1e3, 3), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 1),

@@ -207,25 +207,55 @@ constexpr int kActWinWords = 16384;
 template <int E> constexpr int kActWinExp = E == kF16 ? 8 : 87;
 template <int E> constexpr uint32_t kActWinBase = (uint32_t)kActWinExp<E> << (E == kF16 ? 10 : 7);
 
-template <int E>
-__device__ inline uint32_t lookup_win(const uint16_t* win, const uint16_t* tab, uint32_t x) {
-    const uint32_t d = (x & 0x7fffu) - kActWinBase<E>;
-    return d < 8192u ? (uint32_t)win[((x >> 15) << 13) | d] : (uint32_t)tab[x];
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+
+// Buffer resource over one activation table (kActWords words).
+__device__ inline __amdgpu_buffer_rsrc_t table_rsrc(const uint16_t* tab) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, kActWords * 2, kRsrcWord3);
 }
 
-template <int E>
-__device__ inline u32x4 lookup8_win(const uint16_t* win, const uint16_t* tab, u32x4 x) {
-    u32x4 r;
+// Lookups through the window: the table's word for x comes from the LDS window
+// when the window holds x, else from the table in global memory.  Both reads
+// are issued for every word and neither is branched: the LDS read at its sign's
+// first entry when the window misses, the buffer load at an out-of-range offset
+// (zero, no memory traffic) when it hits.  (A select of the two addresses as
+// one generic pointer had the compiler wait after every two lookups.)
+// The table's words for CH chunks of 8 packed words: every read issued first,
+// then (past a scheduling barrier) the selects, so that the compiler cannot
+// consume each lookup as it goes.  win: the LDS window, or null for none (all
+// words from the table in global memory).
+template <int E, int CH>
+__device__ inline void lookup_chunks(lds_u16* win, __amdgpu_buffer_rsrc_t rt, u32x4 (&t)[CH]) {
+    uint32_t w[CH][8], g[CH][8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = lookup_win<E>(win, tab, x[q] & 0xffffu) | (lookup_win<E>(win, tab, x[q] >> 16) << 16);
-    return r;
-}
-
-__device__ inline u32x4 lookup8(const uint16_t* tab, u32x4 x) {
-    u32x4 r;
+    for (int k = 0; k < CH; ++k)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = (uint32_t)tab[x[q] & 0xffffu] | ((uint32_t)tab[x[q] >> 16] << 16);
-    return r;
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t x = (t[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            if (win) {
+                const uint32_t d = (x & 0x7fffu) - kActWinBase<E>;
+                const bool in = d < 8192u;
+                w[k][e] = win[((x >> 15) << 13) | (in ? d : 0u)];
+                g[k][e] = __builtin_amdgcn_raw_buffer_load_b16(rt, in ? kOOB : 2u * x, 0, 0);
+            } else {
+                g[k][e] = __builtin_amdgcn_raw_buffer_load_b16(rt, 2u * x, 0, 0);
+            }
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * q + h;
+                const uint32_t x = (t[k][q] >> (16 * h)) & 0xffffu;
+                const bool in = win && ((x & 0x7fffu) - kActWinBase<E>) < 8192u;
+                v[h] = in ? w[k][e] : g[k][e];
+            }
+            t[k][q] = v[0] | (v[1] << 16);
+        }
 }
 
 // 8 consecutive words src[0..7] of a row, the valid ones only (col + e < N,
@@ -283,9 +313,9 @@ __device__ inline void epi_apply4(const EpiArgs& ep, uint16_t t[4], const Extras
     for (int s = 0; s < ep.nsteps; ++s) {
         const int op = epi_op(ep, s);
         if (op >= kEpiSilu) {
-            const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
+            const __amdgpu_buffer_rsrc_t rt = table_rsrc(ep.act + (op - kEpiSilu) * kActWords);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = tab[t[e]];
+            for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_raw_buffer_load_b16(rt, 2u * t[e], 0, 0);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

@@ -166,7 +166,7 @@ gemm_kernel(LinearArgs a) {
 // win_op is 0); other activation steps read their tables from global memory.
 template <int BM, int BN, int NT, int E, int MODE>
 __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, int m0, int n0, int tid,
-                                const uint16_t* win = nullptr, int win_op = 0) {
+                                lds_u16* win = nullptr, int win_op = 0) {
     constexpr int CPR = BN / 8;
     constexpr int CHT = BM * CPR / NT;               // chunks per thread
     constexpr int CH = CHT < 8 ? CHT : 8;            // chunks per pass (bounds register use)
@@ -192,14 +192,9 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
         for (int s = 0; MODE == kOutEpi && s < ep.nsteps; ++s) {
             const int op = epi_op(ep, s);
             if (op >= kEpiSilu) {
-                const uint16_t* tab = ep.act + (op - kEpiSilu) * kActWords;
-                if (op == win_op) {
-#pragma unroll
-                    for (int k = 0; k < CH; ++k) t[k] = lookup8_win<E>(win, tab, t[k]);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < CH; ++k) t[k] = lookup8(tab, t[k]);
-                }
+                const __amdgpu_buffer_rsrc_t rt = table_rsrc(ep.act + (op - kEpiSilu) * kActWords);
+                if (op == win_op) lookup_chunks<E, CH>(win, rt, t);
+                else lookup_chunks<E, CH>(nullptr, rt, t);
                 continue;
             }
             u32x4 v[CH];
@@ -514,7 +509,7 @@ gemm_stream(LinearArgs a) {
             }
         if constexpr (MODE == kOutEpi) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x, (const uint16_t*)(smem + TILEB), win_op);
+        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x, (lds_u16*)(smem + TILEB), win_op);
         return;
     }
 

@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--repeats", type=int, default=5, help="timed regions; the median is reported")
+    ap.add_argument("--repeats", type=int, default=1, help="timed regions of --steps steps each; the median is reported")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="time only this workload (profiling runs)")
@@ -183,8 +183,53 @@ def time_region(graph, replays, stream, torch):
     return start.elapsed_time(end)
 
 
+STEPS_PER_GRAPH = 128   # decode steps per captured graph (each replay adds a graph launch of its own)
+
+
+def step_schedule(steps: int, period: int):
+    """How `steps` steps run as graph replays: (full replays of a `period`-step
+    graph, steps in one remainder graph).  Always exactly `steps` steps."""
+    steps = max(0, int(steps))
+    return steps // period, steps % period
+
+
+class StepRunner:
+    """Runs exactly n decode steps as replays of one `period`-step graph plus one
+    remainder graph (captured on first use).  Steps start at step 0 of the weight
+    rotation in each graph; the period is a multiple of the rotation, so whole
+    replays continue it seamlessly."""
+
+    def __init__(self, step, period, stream, torch):
+        self.step, self.period, self.stream, self.torch = step, period, stream, torch
+        self.graphs = {}
+        self.eager_steps = 0   # steps run eagerly while capturing (graph warm-up)
+
+    def graph(self, n):
+        if n not in self.graphs:
+            self.graphs[n] = capture(self.step, n, self.stream, self.torch)
+            self.eager_steps += n
+        return self.graphs[n]
+
+    def prepare(self, *counts):
+        for c in counts:
+            q, r = step_schedule(c, self.period)
+            if q:
+                self.graph(self.period)
+            if r:
+                self.graph(r)
+
+    def run(self, n):
+        q, r = step_schedule(n, self.period)
+        for _ in range(q):
+            self.graph(self.period).replay()
+        if r:
+            self.graph(r).replay()
+
+
 def bench_decode(args, torch, la, workloads, stream, dtype=None):
-    """The step: one call at M=1 and one at M=16.  Returns (ms_per_step, detail)."""
+    """The step: one call at M=1 and one at M=16.  Exactly args.warmup untimed
+    steps, then timed regions of exactly args.steps steps each (args.repeats of
+    them, the median reported; one by default).  Returns (ms_per_step, detail)."""
     dtype = dtype or torch.float16
     fn = la.linear_bf16 if dtype == torch.bfloat16 else la.linear_f16
     w1, w16 = workloads.WORKLOADS["gemv1"], workloads.WORKLOADS["gemv16"]
@@ -200,30 +245,53 @@ def bench_decode(args, torch, la, workloads, stream, dtype=None):
         fn(x1, weights[(2 * i) % copies], b, out=y1, stream=stream)
         fn(x16, weights[(2 * i + 1) % copies], b, out=y16, stream=stream)
 
-    # One graph holds `period` steps: a multiple of copies / 2, so every weight copy
-    # is used equally, and as many steps as divide the request, up to 128 (each
-    # replay adds a graph launch of its own: 8 steps per graph measured 3% more
-    # per launch than 128).
+    # a graph of a fixed number of steps, a multiple of copies / 2 so that whole
+    # replays use every weight copy equally: the per-replay graph launch is then
+    # the same fraction of a step whatever --steps asks for
     base = max(1, copies // 2)
-    period = next((p for p in range(base * 16, base - 1, -base) if args.steps % p == 0), base)
-    graph = capture(step, period, stream, torch)
-    replays = max(1, args.steps // period)
-    steps = replays * period
-    for _ in range(max(1, args.warmup // period)):
-        graph.replay()
-    times = [time_region(graph, replays, stream, torch) for _ in range(args.repeats)]
-    ms = sorted(times)[len(times) // 2] / steps
-    args.steps = steps
+    period = max(base, (STEPS_PER_GRAPH // base) * base)
+    runner = StepRunner(step, period, stream, torch)
+    runner.prepare(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    runner.run(args.warmup)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, args.repeats)):
+        times.append(time_steps(runner, args.steps, stream, torch))
+    ms = sorted(times)[len(times) // 2] / max(1, args.steps)
+    q, r = step_schedule(args.steps, period)
     plan = la.linear_f16_plan(x16, wbase, b)
     detail = {
         "step_bytes": step_bytes,
         "weight_copies": copies,
         "steps_per_graph": period,
-        "ms_per_step_all": [t / steps for t in times],
+        "graph_replays": {"full": q, "remainder_steps": r},
+        "timed_regions": len(times),
+        "eager_steps_at_capture": runner.eager_steps,
+        "ms_per_step_all": [t / max(1, args.steps) for t in times],
         "plan_m16": plan,
         "plan_m1": la.linear_f16_plan(x1, wbase, b),
     }
+    del runner
+    torch.cuda.synchronize()
     return ms, detail
+
+
+def time_steps(runner, steps, stream, torch):
+    """Exactly `steps` steps between two HIP events on `stream`, with the device
+    synchronised on both sides; returns ms.  A region carries a fixed cost of
+    about 10 us (its graphs' launch boundaries and the first steps after the idle
+    device), 2.5-3% of a 20-step region and under 0.1% of a 2000-step one."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        runner.run(steps)
+        end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
 
 
 def bench_context(torch, la, workloads, stream):
@@ -396,6 +464,77 @@ def bench_indexed(name, torch, la, workloads, stream, calls, dtype_name="f16"):
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "input_sets": sets}
 
 
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_amd", "liblinear_probe.so"))
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.probe_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.probe_empty.argtypes = [i32, vp]
+    lib.probe_mfma.argtypes = [vp, i32, i32, vp, vp]
+    for f in (lib.probe_read, lib.probe_empty, lib.probe_mfma):
+        f.restype = i32
+    return lib
+
+
+def bench_probe(kind, torch, workloads, stream):
+    """Ceilings for the kernels' roofline fractions, measured with the probe
+    kernels of liblinear_probe.so in graphs of 64 launches:
+      read:  a plain read of the decode weight ([4096, 4096] binary16, 32 MiB),
+             rotating over the same 16 copies as the decode benchmark, on the
+             decode kernel's grid (256 workgroups of 512 threads);
+      empty: an empty kernel on that grid (the per-launch floor);
+      mfma:  register-only v_mfma_f32_32x32x16_f16 on random binary16 operands
+             (1024 workgroups of 4 waves, 2000 rounds of 8 MFMAs per wave)."""
+    lib = _probe_lib()
+    sp = ctypes_stream(stream)
+    if kind == "read":
+        _, w, _ = workloads.workload_inputs("gemv1", seed=0, device="cuda")
+        copies = rotation_sets(w.numel() * 2)
+        ws = [w] + [w.clone() for _ in range(copies - 1)]
+        sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        nbytes = w.numel() * 2
+
+        def call(i):
+            rc = lib.probe_read(ws[i % copies].data_ptr(), nbytes, 256, sink.data_ptr(), sp)
+            assert rc == 0, rc
+        calls, per = graph_calls(copies), nbytes
+    elif kind == "empty":
+        def call(i):
+            assert lib.probe_empty(256, sp) == 0
+        calls, per = 64, 0
+    elif kind == "mfma":
+        g = torch.Generator(device="cpu").manual_seed(3)
+        ops = torch.randn(4096 * 64 * 8, generator=g).to(torch.float16).to("cuda")
+        grid, iters = 1024, 2000
+        out = torch.empty(grid * 4 * 64 * 64, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            assert lib.probe_mfma(ops.data_ptr(), grid, iters, out.data_ptr(), sp) == 0
+        calls, per = 8, 0
+    else:
+        raise SystemExit("unknown probe %s" % kind)
+    graph = capture(call, calls, stream, torch)
+    graph.replay()
+    replays = max(1, 640 // calls) if kind != "mfma" else 4
+    times = [time_region(graph, replays, stream, torch) for _ in range(5)]
+    us = sorted(times)[2] / (replays * calls) * 1e3
+    del graph
+    torch.cuda.synchronize()
+    r = {"probe": kind, "us_per_launch": round(us, 3)}
+    if kind == "read":
+        r.update({"bytes_per_launch": per, "gbs": round(per / (us * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(per / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": copies})
+    if kind == "mfma":
+        flops = grid * 4 * iters * 8 * 32768.0
+        r.update({"flops_per_launch": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                  "frac_mfma_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)})
+    return r
+
+
+def ctypes_stream(stream):
+    return stream.cuda_stream if stream is not None else None
+
+
 def cpu_baseline(workloads, target_s: float = 12.0):
     """The CPU oracle on the same decode step, repeated for ~target_s of wall time
     (a bounded sample of the workload; its rate is scaled to GB/s per step)."""
@@ -425,6 +564,44 @@ def cpu_baseline(workloads, target_s: float = 12.0):
     }
 
 
+def cpu_baseline_gemm(name, workloads, target_s: float = 2.5):
+    """The CPU oracle on one prefill shape, timed on a bounded sample: the first R
+    rows of x against the whole weight and bias (R x N outputs, full K), R sized
+    for about target_s of wall time (the toy runs whole).  Its rate is scaled to
+    TFLOP/s of the full shape's 2MNK."""
+    import oracle
+    orc = oracle.default()
+    wl = workloads.WORKLOADS[name]
+    x, w, b = workloads.workload_inputs(name, seed=0)
+    step = max(1, orc.max_threads())
+    rows = min(wl.M, step)
+    while True:
+        # grow the sample until one call takes a quarter of the target, then size
+        # the timed call from that rate
+        t0 = time.perf_counter()
+        orc.linear(x[:rows], w, b)
+        el = time.perf_counter() - t0
+        if rows == wl.M or el >= target_s / 4:
+            break
+        rows = min(wl.M, rows * 2)
+    want = min(wl.M, max(rows, int(rows * target_s / max(el, 1e-9)) // step * step))
+    if want != rows:
+        rows = want
+        t0 = time.perf_counter()
+        orc.linear(x[:rows], w, b)
+        el = time.perf_counter() - t0
+    flops = 2.0 * rows * wl.N * wl.K
+    return {
+        "value": round(flops / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d rows of x against the full weight [%d, %d] and b, %.2f s wall%s"
+                  % (rows, wl.M, wl.N, wl.K, el, " (the whole shape)" if rows == wl.M else ""),
+        "full_shape_s_estimate": round(el * wl.M / rows, 2),
+    }
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -438,6 +615,9 @@ def main():
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <COPY_WRITE_DIR> -- python3 bench.py --only copycal",
         ])
         return
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library runs each call on one GPU and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -467,6 +647,8 @@ def main():
             dt = torch.bfloat16 if args.variant == "bf16" else torch.float16
             ms, _ = bench_decode(args, torch, la, workloads, stream, dt)
             log("decode ms/step %.5f" % ms)
+        elif args.only.startswith("probe_"):
+            log(json.dumps(bench_probe(args.only[len("probe_"):], torch, workloads, stream)))
         elif args.only == "context":
             log(json.dumps(bench_context(torch, la, workloads, stream)))
         elif args.only in workloads.GROUPED:
@@ -487,6 +669,9 @@ def main():
     achieved = per_launch_bytes / per_launch_s / 1e9
     log("decode: %.3f us/step, %.1f GB/s" % (ms * 1e3, value))
     context = bench_context(torch, la, workloads, stream)
+    for kind in ("read", "empty", "mfma"):
+        log("probe", kind)
+        context["probe_" + kind] = bench_probe(kind, torch, workloads, stream)
     log("context", json.dumps(context))
 
     prefill = {}
@@ -522,6 +707,9 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(workloads)
         log(json.dumps(cpu))
+        for name in prefill:
+            prefill[name]["cpu_baseline"] = r = cpu_baseline_gemm(name, workloads)
+            log(name, json.dumps(r))
 
     line = {
         "metric": "TFLOP/s and % FP16 MFMA peak (large M); HBM GB/s and % peak (M≤16)",
@@ -543,6 +731,12 @@ def main():
             "calls_per_step": launches,
             "weight_copies_rotated": detail["weight_copies"],
             "steps_per_graph": detail["steps_per_graph"],
+            "timed_as": "%d replays of the %d-step graph + one %d-step graph, between two events, "
+                        "device synchronised on both sides" % (detail["graph_replays"]["full"],
+                                                               detail["steps_per_graph"],
+                                                               detail["graph_replays"]["remainder_steps"]),
+            "warmup_as": "%d steps replayed through the same graphs (plus %d steps run eagerly while "
+                         "capturing them)" % (args.warmup, detail["eager_steps_at_capture"]),
             "kernel": "skinny_stream<8, f16, bias> (16 output columns x 16 rows per workgroup, 8 waves, "
                       "v_mfma_f32_16x16x32_f16)",
         },

@@ -51,7 +51,14 @@
 extern "C" {
 #endif
 
-/* Status codes. */
+/*
+ * Status codes.  Every entry point returns one: a call the library cannot run is
+ * refused with a typed error before anything is enqueued, never a crash or an
+ * abort, as the pages' builder refuses ill-formed ops with a typed error rather
+ * than a panic ("Tracing a Model", section "The Builder and Traced handles";
+ * "The Graph IR", section "Graph structure": shapes and dtypes are checked when
+ * an op is added).
+ */
 #define LINEAR_OK         0
 #define LINEAR_E_NULL     1  /* a required pointer is NULL (only when the output is non-empty) */
 #define LINEAR_E_SHAPE    2  /* M, N or K negative, or beyond the limits above */
@@ -64,7 +71,14 @@ extern "C" {
 #define LINEAR_E_CAPTURE  9  /* the first activation epilogue on a device was called under stream capture */
 #define LINEAR_E_WORKSPACE 10 /* indexed contraction: workspace misaligned or below linear_indexed_workspace_bytes */
 
-/* Path selectors for linear_f16_ex / linear_f16_plan. */
+/*
+ * Path selectors for linear_f16_ex / linear_f16_plan.  The path and the tile are
+ * chosen on the host from the static shapes before any launch: the op table
+ * treats GEMV and GEMM as one MatMul op specialised when the call is planned, and
+ * shapes are inferred on the host ("The Graph IR", op table, MatMul row, and
+ * section "Host-side shape inference").  AUTO is that specialisation; the forced
+ * paths give results within the same contract.
+ */
 #define LINEAR_PATH_AUTO   0  /* M <= 16: skinny path; otherwise the MFMA tiled GEMM */
 #define LINEAR_PATH_GEMM   1  /* force the MFMA tiled GEMM (any M) */
 #define LINEAR_PATH_SKINNY 2  /* force the weight-streaming skinny path (any M, 16 rows per block) */
@@ -313,7 +327,11 @@ int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx,
                                    int64_t E, int64_t M, int64_t N, int64_t K,
                                    void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Which kernels a call would launch.  Pure host function: touches no device.
+/* Which kernels a call would launch: the host-side plan of "The Graph IR" (op
+ * table, MatMul row: GEMV versus GEMM chosen at plan time; section "Host-side
+ * shape inference").  Enqueues nothing and touches no device memory; the tile
+ * rules count the compute units of the current device when a gfx950 is current
+ * (a partitioned part has fewer), else those of a whole MI355X (256).
  * A GEMM call whose largest tiles would leave a last wave of workgroups at most
  * half full over the GPU's CUs is split by output columns into two launches of
  * the same kernel family: columns [0, split_n) in whole waves of the first tile,

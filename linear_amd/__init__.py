@@ -399,8 +399,10 @@ def indexed_workspace_bytes(E: int, M: int) -> int:
     return n
 
 
-def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
-    """x [M, K], w [E, K, N] (inner two dims row-major), idx [M] int32."""
+def _indexed_args(dtype, x, w, idx, out, f32):
+    """Checks and marshalling shared by the indexed calls: x [M, K], w [E, K, N]
+    (inner two dims row-major), idx [M] int32.  Returns (out, pointer/stride/shape
+    arguments of the C call up to K)."""
     if x.dtype != dtype or w.dtype != dtype:
         raise TypeError("x and w must be %s" % dtype)
     if idx.dtype != torch.int32 or idx.dim() != 1 or (idx.shape[0] > 1 and idx.stride(0) != 1):
@@ -422,6 +424,12 @@ def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
     yp, ldy = _mat(out, "out", out_dtype)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [%d, %d]" % (M, N))
+    return out, (xp, ldx, w.data_ptr(), ldw, sw, idx.data_ptr(), yp, ldy, E, M, N, K)
+
+
+def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
+    out, args = _indexed_args(dtype, x, w, idx, out, f32)
+    E, M = args[8], args[9]
     need = indexed_workspace_bytes(E, M)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
@@ -429,8 +437,7 @@ def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
         raise ValueError("workspace must be a uint8 tensor of at least %d bytes" % need)
     tag = "bf16" if dtype == torch.bfloat16 else "f16"
     name = "linear_%s_indexed%s" % (tag, "_f32out" if f32 else "")
-    rc = getattr(_lib(), name)(xp, ldx, w.data_ptr(), ldw, sw, idx.data_ptr(), yp, ldy, E, M, N, K,
-                               workspace.data_ptr(), workspace.numel(),
+    rc = getattr(_lib(), name)(*args, workspace.data_ptr(), workspace.numel(),
                                _stream_handle(stream, x, w, idx, out, workspace))
     _check(rc, name)
     return out

@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblinear_amd.so")
+# measurement kernels for bench.py's ceilings, kept out of the layer's library
+PROBE_OUT = os.path.join(HERE, "liblinear_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "skinny.hip", "epilogue.hip", "indexed.hip", "linear_abi.hip"]
@@ -86,16 +89,18 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     # a failed build must not leave the previous library behind for tests and
     # benchmarks to load
-    if os.path.exists(OUT):
-        os.remove(OUT)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
-    if verbose:
-        print("built", OUT)
+    for out in (OUT, PROBE_OUT):
+        if os.path.exists(out):
+            os.remove(out)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    for out, part in ((OUT, objs[:len(SOURCES)]), (PROBE_OUT, objs[len(SOURCES):])):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *part, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+        if verbose:
+            print("built", out)
     return OUT
 
 

@@ -50,6 +50,7 @@ struct LinearArgs {
     EpiArgs epi;         // the epilogue program (kOutEpi only)
     int64_t gsx, gsy;    // grouped calls (gridDim.z groups): x and y group strides in elements
     int groups;          // gridDim.z (1 for ungrouped calls)
+    int xcd_shift;       // log2 of the device's XCD count (workgroup ids are dealt round-robin over them)
 };
 
 

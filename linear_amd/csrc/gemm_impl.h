@@ -22,7 +22,7 @@
 //    resources whose range ends at the matrix's last valid element, so rows past
 //    M or N and K chunks past K read as zero; stores are masked.
 //  - Workgroup ids are remapped so that each XCD (consecutive ids are dealt
-//    round-robin over the 8 XCDs) owns a contiguous run of tiles, walked in
+//    round-robin over the device's XCDs) owns a contiguous run of tiles, walked in
 //    groups of 4 tile-rows, so tiles running together share x and weight panels
 //    in that XCD's L2.
 // The streaming kernel (aligned layouts) and the register-staged one (any
@@ -63,7 +63,7 @@ gemm_kernel(LinearArgs a) {
     __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
     int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = a.K;
 
@@ -277,7 +277,7 @@ gemm_stream(LinearArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDSB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = a.K;
     const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n0, a.N, a.ldw, K);

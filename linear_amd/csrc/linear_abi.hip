@@ -25,7 +25,15 @@ constexpr int64_t kMaxLdOut = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxGridX = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxGridY = 65535;
 constexpr int kSkinnyMaxM = 16;   // AUTO sends M <= 16 to the skinny path
-constexpr int kNumCUs = 256;
+
+// The compute units and XCDs of the device a call runs on, read from the device
+// (a partitioned part has fewer).  Plans made without a usable device (the
+// pure-host linear_f16_plan) assume a whole MI355X: 256 CUs in 8 XCDs.
+struct DevInfo {
+    int cus;
+    int xcd_shift;   // log2 of the XCD count; 0 (no XCD-aware remap) when not a power of two
+};
+constexpr DevInfo kWholeMI355X{256, 3};
 
 struct Extent {
     uintptr_t lo, hi;  // [lo, hi) in bytes; hi == lo when empty
@@ -142,10 +150,10 @@ bool vector_store_ok(const Request& r) {
 
 // Tile choice for the register-staged kernel (unaligned layouts, not tuned): the
 // larger tile when it still gives every CU a tile.  Tiles count over all G groups.
-int choose_gemm_config(int64_t M, int64_t N, int64_t G) {
+int choose_gemm_config(int64_t M, int64_t N, int64_t G, int cus) {
     const lin::GemmConfig& g = lin::kGemmConfigs[0];
     const int64_t tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn) * G;
-    return tiles >= kNumCUs ? 0 : 1;
+    return tiles >= cus ? 0 : 1;
 }
 
 // Tile choice for the streaming kernel (aligned layouts).  Measured on MI355X, a
@@ -160,7 +168,7 @@ struct StreamChoice {
 // kStreamConfigs in order: 256x256, 256x128, 128x256, 128x128, 64x64
 const StreamChoice kStreamOrder[] = {{0, 1.00}, {1, 0.94}, {2, 0.85}, {3, 0.80}, {4, 0.57}};
 
-int choose_stream_config(int64_t M, int64_t N, int64_t G) {
+int choose_stream_config(int64_t M, int64_t N, int64_t G, int cus) {
     int best = 4;
     double best_score = -1.0;
     for (const StreamChoice& c : kStreamOrder) {
@@ -168,7 +176,7 @@ int choose_stream_config(int64_t M, int64_t N, int64_t G) {
         const int64_t per_group = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
         if (per_group > kMaxGridX / 64) continue;
         const int64_t tiles = per_group * G;
-        if (tiles >= kNumCUs) return c.cfg;
+        if (tiles >= cus) return c.cfg;
         const double score = (double)tiles * c.rate;
         if (score > best_score) {
             best_score = score;
@@ -191,25 +199,25 @@ struct ColumnSplit {
     int cfg2;
 };
 
-ColumnSplit column_split(int64_t M, int64_t N, int64_t G, int cfg) {
+ColumnSplit column_split(int64_t M, int64_t N, int64_t G, int cfg, int cus) {
     ColumnSplit sp{0, 0};
     if (G != 1 || cfg != 0) return sp;
     const lin::GemmConfig& g = lin::kStreamConfigs[cfg];
     const int64_t tm = (M + g.bm - 1) / g.bm, tn = (N + g.bn - 1) / g.bn;
-    const int64_t tiles = tm * tn, last = tiles % kNumCUs;
-    if (tiles <= kNumCUs || last == 0 || last > kNumCUs / 2) return sp;
+    const int64_t tiles = tm * tn, last = tiles % cus;
+    if (tiles <= cus || last == 0 || last > cus / 2) return sp;
     // the most column tiles short of tn that make whole waves
     for (int64_t t = tn - 1; t > 0; --t) {
-        if ((tm * t) % kNumCUs == 0) {
+        if ((tm * t) % cus == 0) {
             sp.n0 = t * g.bn;
-            sp.cfg2 = choose_stream_config(M, N - sp.n0, 1);
+            sp.cfg2 = choose_stream_config(M, N - sp.n0, 1, cus);
             return sp;
         }
     }
     return sp;
 }
 
-int32_t plan(const Request& r, linear_plan* p) {
+int32_t plan(const Request& r, linear_plan* p, int cus) {
     memset(p, 0, sizeof *p);
     int32_t path = r.path;
     if (path == LINEAR_PATH_AUTO) path = (r.M <= kSkinnyMaxM) ? LINEAR_PATH_SKINNY : LINEAR_PATH_GEMM;
@@ -225,7 +233,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         p->grid = gx * gy * r.G;
     } else {
         const bool stream = p->vector_io != 0;
-        const int c = stream ? choose_stream_config(r.M, r.N, r.G) : choose_gemm_config(r.M, r.N, r.G);
+        const int c = stream ? choose_stream_config(r.M, r.N, r.G, cus) : choose_gemm_config(r.M, r.N, r.G, cus);
         const lin::GemmConfig& g = stream ? lin::kStreamConfigs[c] : lin::kGemmConfigs[c];
         p->tile_m = g.bm;
         p->tile_n = g.bn;
@@ -235,7 +243,7 @@ int32_t plan(const Request& r, linear_plan* p) {
         if (p->grid > kMaxGridX / 64) return LINEAR_E_SHAPE;
         p->grid *= r.G;
         if (stream) {
-            const ColumnSplit sp = column_split(r.M, r.N, r.G, c);
+            const ColumnSplit sp = column_split(r.M, r.N, r.G, c, cus);
             if (sp.n0 > 0) {
                 const lin::GemmConfig& g2 = lin::kStreamConfigs[sp.cfg2];
                 p->grid = ((r.M + g.bm - 1) / g.bm) * (sp.n0 / g.bn);
@@ -249,9 +257,13 @@ int32_t plan(const Request& r, linear_plan* p) {
     return LINEAR_OK;
 }
 
-// Device check, cached per device: the current device must be a gfx950.
-int32_t check_device(int* dev_out) {
-    static std::atomic<int> cached[64];  // 0 unknown, 1 gfx950, 2 other (callers may be on several threads)
+// Device check, cached per device: the current device must be a gfx950.  Also
+// caches its compute units and XCDs for the tile rules and the tile remap.
+int32_t check_device(int* dev_out, DevInfo* info = nullptr) {
+    // per device: 0 unknown, 1 gfx950, 2 other (callers may be on several threads);
+    // the CU and XCD figures are stored before the state is published
+    static std::atomic<int> cached[64];
+    static std::atomic<int> cus[64], xcd_shift[64];
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0) {
@@ -265,11 +277,30 @@ int32_t check_device(int* dev_out) {
             g_last_hip_error = (int32_t)e;
             return LINEAR_E_DEVICE;
         }
+        int xcds = 1;
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) xcds = 1;
+        int shift = 0;
+        while ((2 << shift) <= xcds) ++shift;
+        if ((1 << shift) != xcds) shift = 0;   // not a power of two: no XCD-aware remap
+        cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kWholeMI355X.cus;
+        xcd_shift[dev] = shift;
         cached[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
     }
     if (dev >= 64 || cached[dev] != 1) return LINEAR_E_DEVICE;
     *dev_out = dev;
+    if (info) *info = DevInfo{cus[dev], xcd_shift[dev]};
     return LINEAR_OK;
+}
+
+// The current device's figures when a usable device is current, else a whole
+// MI355X's (leaves the thread's last HIP error as it was).
+DevInfo current_device_or_whole_part() {
+    const int32_t saved = g_last_hip_error;
+    int dev = 0;
+    DevInfo info = kWholeMI355X;
+    if (check_device(&dev, &info) != LINEAR_OK) info = kWholeMI355X;
+    g_last_hip_error = saved;
+    return info;
 }
 
 int32_t run(const Request& r, void* stream) {
@@ -277,11 +308,16 @@ int32_t run(const Request& r, void* stream) {
     if (st != LINEAR_OK) return st;
     if (r.M == 0 || r.N == 0 || r.G == 0) return LINEAR_OK;
     linear_plan p;
-    st = plan(r, &p);
+    st = plan(r, &p, kWholeMI355X.cus);   // shape errors come before device errors
     if (st != LINEAR_OK) return st;
     int dev = 0;
-    st = check_device(&dev);
+    DevInfo di = kWholeMI355X;
+    st = check_device(&dev, &di);
     if (st != LINEAR_OK) return st;
+    if (di.cus != kWholeMI355X.cus) {
+        st = plan(r, &p, di.cus);
+        if (st != LINEAR_OK) return st;
+    }
 
     lin::LinearArgs a;
     a.x = r.x;
@@ -296,6 +332,7 @@ int32_t run(const Request& r, void* stream) {
     a.K = (int)r.K;
     a.vec_store = vector_store_ok(r) ? 1 : 0;
     a.groups = (int)r.G;
+    a.xcd_shift = di.xcd_shift;
     a.gsx = r.sx;
     a.gsy = r.sy;
     memset(&a.epi, 0, sizeof a.epi);
@@ -335,11 +372,11 @@ int32_t run(const Request& r, void* stream) {
         a.tiles_n = (int)((r.N + 15) / 16);
         e = lin::launch_skinny(r.elem, a, vec, mode, (hipStream_t)stream);
     } else if (vec) {
-        const int c = choose_stream_config(r.M, r.N, r.G);
+        const int c = choose_stream_config(r.M, r.N, r.G, di.cus);
         const lin::GemmConfig& g = lin::kStreamConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
-        const ColumnSplit sp = column_split(r.M, r.N, r.G, c);
+        const ColumnSplit sp = column_split(r.M, r.N, r.G, c, di.cus);
         if (sp.n0 == 0) {
             e = lin::launch_gemm_stream(r.elem, c, a, mode, (hipStream_t)stream);
         } else {
@@ -365,7 +402,7 @@ int32_t run(const Request& r, void* stream) {
             }
         }
     } else {
-        const int c = choose_gemm_config(r.M, r.N, r.G);
+        const int c = choose_gemm_config(r.M, r.N, r.G, di.cus);
         const lin::GemmConfig& g = lin::kGemmConfigs[c];
         a.tiles_m = (int)((r.M + g.bm - 1) / g.bm);
         a.tiles_n = (int)((r.N + g.bn - 1) / g.bn);
@@ -411,7 +448,8 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
         (K > 0 && overlaps(ew, extent_g(w, E, sw, K, ldw, N))))
         return LINEAR_E_ALIAS;
     int dev = 0;
-    int32_t st = check_device(&dev);
+    DevInfo di = kWholeMI355X;
+    int32_t st = check_device(&dev, &di);
     if (st != LINEAR_OK) return st;
     lin::IndexedArgs a;
     a.x = x;
@@ -442,7 +480,7 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
         a.slots = (int)((M + g0.bm - 1) / g0.bm + std::min(E, M));
         const int64_t grid = (int64_t)a.slots * ((N + g0.bn - 1) / g0.bn);
         if (grid > kMaxGridX) return LINEAR_E_SHAPE;
-        if (cfg == 0 && M <= lin::kIdxSelfRouteRows && grid <= 2 * kNumCUs) cfg = 2;
+        if (cfg == 0 && M <= lin::kIdxSelfRouteRows && grid <= 2 * di.cus) cfg = 2;
         e = lin::launch_indexed_routed(elem, cfg, a, mode, (hipStream_t)stream);
     } else {
         e = lin::launch_indexed(elem, a, mode, (hipStream_t)stream);
@@ -601,7 +639,7 @@ int32_t linear_f16_plan(const uint16_t* x, int64_t ldx, const uint16_t* weight, 
         out->path = path == LINEAR_PATH_AUTO ? LINEAR_PATH_SKINNY : path;
         return LINEAR_OK;
     }
-    return plan(r, out);
+    return plan(r, out, current_device_or_whole_part().cus);
 }
 
 const char* linear_status_string(int32_t status) {

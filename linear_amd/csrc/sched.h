@@ -7,15 +7,17 @@
 namespace lin {
 
 // Tile (tm, tn) of workgroup bid in a tiles_m x tiles_n grid.  Consecutive
-// workgroup ids are dealt round-robin over the 8 XCDs, so each XCD is given a
-// contiguous run of tiles, walked in groups of 4 tile-rows: tiles running
+// workgroup ids are dealt round-robin over the device's 2^xcd_shift XCDs (8 on
+// a whole MI355X; the host reads the count from the device), so each XCD is
+// given a contiguous run of tiles, walked in groups of 4 tile-rows: tiles running
 // together on one XCD share operand panels in its L2.  With 32 tiles at a time
 // per XCD that is 4 x panels and 8 weight panels; x panels cost more L2 misses
 // per panel, and 4 rows measured faster than 2, 8 or 16.
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int xcd_shift, int& tm, int& tn) {
     const int G = tiles_m * tiles_n;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int q = G >> 3, r = G & 7;
+    const int xmask = (1 << xcd_shift) - 1;
+    const int xcd = bid & xmask, idx = bid >> xcd_shift;
+    const int q = G >> xcd_shift, r = G & xmask;
     const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
     constexpr int GROUP = 4;
     const int per_group = GROUP * tiles_n;

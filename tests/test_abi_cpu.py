@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 11):
         assert la.linear_status_string(code) != "unknown status"
     assert la.linear_status_string(99) == "unknown status"
 

@@ -87,3 +87,40 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+class _FakeGraph:
+    def __init__(self, fn, calls, log):
+        self.fn, self.calls, self.log = fn, calls, log
+
+    def replay(self):
+        for i in range(self.calls):
+            self.fn(i)
+
+
+@pytest.mark.parametrize("steps,warmup", [(20, 5), (2000, 200), (1, 0), (128, 128), (129, 3), (300, 7)])
+def test_decode_steps_run_exactly_as_requested(monkeypatch, steps, warmup):
+    """The timed region runs exactly --steps steps and the warm-up exactly --warmup
+    steps, whatever the graph size (whole replays plus one remainder graph), and
+    every replayed step continues the weight rotation from step 0."""
+    ran = []
+    monkeypatch.setattr(bench, "capture", lambda fn, calls, stream, torch: _FakeGraph(fn, calls, ran))
+    period = 128
+    runner = bench.StepRunner(lambda i: ran.append(i), period, None, None)
+    runner.prepare(warmup, steps)
+    ran.clear()
+    runner.run(warmup)
+    assert len(ran) == warmup
+    ran.clear()
+    runner.run(steps)
+    assert len(ran) == steps
+    q, r = bench.step_schedule(steps, period)
+    assert q * period + r == steps and 0 <= r < period
+    # whole replays each run steps 0 .. period-1, the remainder 0 .. r-1
+    assert ran == list(range(period)) * q + list(range(r))
+
+
+def test_bad_step_counts_are_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "--steps" in r.stderr

@@ -70,6 +70,7 @@ extern "C" {
 #define LINEAR_E_EPILOGUE 8  /* epilogue program: step count outside 0..LINEAR_EPI_MAX_STEPS or an unknown step */
 #define LINEAR_E_CAPTURE  9  /* the first activation epilogue on a device was called under stream capture */
 #define LINEAR_E_WORKSPACE 10 /* indexed contraction: workspace misaligned or below linear_indexed_workspace_bytes */
+#define LINEAR_E_SCRATCH  11  /* linear_f16_indexed_noalloc: the call needs more than LINEAR_NOALLOC_SCRATCH_BYTES */
 
 /*
  * Path selectors for linear_f16_ex / linear_f16_plan.  The path and the tile are
@@ -326,6 +327,31 @@ int32_t linear_bf16_indexed_f32out(const uint16_t* x, int64_t ldx,
                                    float* y, int64_t ldy,
                                    int64_t E, int64_t M, int64_t N, int64_t K,
                                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): linear_f16_indexed
+ * without the workspace argument.  Same arguments otherwise, same kernels, same
+ * results bit for bit, same errors, except that the row-to-expert binning goes
+ * into a scratch array of LINEAR_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory (one per GPU, from the first such call on that GPU until the
+ * process ends).  A call whose binning needs more, i.e.
+ * linear_indexed_workspace_bytes(E, M) > LINEAR_NOALLOC_SCRATCH_BYTES (about
+ * 200,000 rows at a few experts), returns LINEAR_E_SCRATCH with nothing
+ * enqueued.  The call allocates nothing and frees nothing; nothing in the
+ * scratch array needs clearing between calls (each call's routing pass writes
+ * every word its kernels read).  All such calls on one GPU share that GPU's
+ * array: two of them in flight at once on that GPU (on different streams, or
+ * captured graphs replayed concurrently) race and may give wrong results; calls
+ * in one stream's order are safe.
+ */
+#define LINEAR_NOALLOC_SCRATCH_BYTES (1 << 20)
+int32_t linear_f16_indexed_noalloc(const uint16_t* x, int64_t ldx,
+                                   const uint16_t* w, int64_t ldw, int64_t sw,
+                                   const int32_t* idx,
+                                   uint16_t* y, int64_t ldy,
+                                   int64_t E, int64_t M, int64_t N, int64_t K,
+                                   void* stream);
 
 /* Which kernels a call would launch: the host-side plan of "The Graph IR" (op
  * table, MatMul row: GEMV versus GEMM chosen at plan time; section "Host-side

@@ -29,6 +29,10 @@ LINEAR_E_LAUNCH = 7
 LINEAR_E_EPILOGUE = 8
 LINEAR_E_CAPTURE = 9
 LINEAR_E_WORKSPACE = 10
+LINEAR_E_SCRATCH = 11
+
+# scratch the no-allocation indexed call holds per GPU (include/linear_amd.h)
+NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # Epilogue steps (include/linear_amd.h, LINEAR_EPI_*)
 EPI_MAX_STEPS = 8
@@ -49,6 +53,7 @@ ENTRY_POINTS = ("linear_f16", "linear_f16_nobias", "linear_f16_ex", "linear_f16_
                 "linear_f16_grouped", "linear_bf16_grouped", "linear_f16_grouped_f32out", "linear_bf16_grouped_f32out",
                 "linear_indexed_workspace_bytes",
                 "linear_f16_indexed", "linear_bf16_indexed", "linear_f16_indexed_f32out", "linear_bf16_indexed_f32out",
+                "linear_f16_indexed_noalloc",
                 "linear_f16_plan", "linear_status_string", "linear_last_hip_error")
 
 
@@ -120,6 +125,8 @@ def _lib():
                  "linear_bf16_indexed_f32out"):
         getattr(lib, name).argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp]
         getattr(lib, name).restype = i32
+    lib.linear_f16_indexed_noalloc.argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.linear_f16_indexed_noalloc.restype = i32
     lib.linear_indexed_workspace_bytes.argtypes = [i64, i64]
     lib.linear_indexed_workspace_bytes.restype = i64
     lib.linear_f16_plan.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, i32,
@@ -440,6 +447,19 @@ def _indexed_call(dtype, x, w, idx, out, f32, stream, workspace):
     rc = getattr(_lib(), name)(*args, workspace.data_ptr(), workspace.numel(),
                                _stream_handle(stream, x, w, idx, out, workspace))
     _check(rc, name)
+    return out
+
+
+def linear_f16_indexed_noalloc(x, w, idx, out, stream=None):
+    """linear_f16_indexed without a workspace, for callers that cannot allocate: the
+    library's per-GPU scratch array (NOALLOC_SCRATCH_BYTES) holds the routing.
+    out must be given (a [M, N] binary16 tensor; this call allocates nothing).
+    Calls in flight at once on one GPU share that array and race."""
+    if out is None:
+        raise ValueError("out is required: the no-allocation call creates no tensor")
+    out, args = _indexed_args(torch.float16, x, w, idx, out, False)
+    rc = _lib().linear_f16_indexed_noalloc(*args, _stream_handle(stream, x, w, idx, out))
+    _check(rc, "linear_f16_indexed_noalloc")
     return out
 
 

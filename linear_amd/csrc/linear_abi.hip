@@ -492,9 +492,51 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     return LINEAR_OK;
 }
 
+// The no-allocation indexed entry point's routing scratch: one array per GPU,
+// held from the library's load until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol, never a device address: kernels
+// get the address that hipGetSymbolAddress returns for the current device,
+// looked up once per device at that device's first such call.
+constexpr int64_t kNoAllocScratchBytes = LINEAR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes % 16 == 0, "the workspace must stay 16-byte sized");
+
+// This device's address of `scratch` (dev current), or null with the HIP error kept.
+void* scratch_address(int dev) {
+    static std::atomic<void*> addr[64];   // per device; calls may come from several host threads
+    if (dev < 0 || dev >= 64) return nullptr;
+    void* p = addr[dev].load();
+    if (p) return p;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        g_last_hip_error = (int32_t)e;
+        return nullptr;
+    }
+    addr[dev].store(p);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t linear_f16_indexed_noalloc(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t sw,
+                                   const int32_t* idx, uint16_t* y, int64_t ldy, int64_t E, int64_t M, int64_t N,
+                                   int64_t K, void* stream) {
+    // the workspace call's own checks decide shapes and no-ops; only a call that
+    // would launch needs the scratch, and it must fit
+    if (M < 0 || N < 0 || K < 0 || E < 0) return LINEAR_E_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || E > kMaxGridY) return LINEAR_E_SHAPE;
+    if (M == 0 || N == 0 || E == 0) return LINEAR_OK;
+    if (lin::idx_ws_bytes(E, M) > kNoAllocScratchBytes) return LINEAR_E_SCRATCH;
+    int dev = 0;
+    const int32_t st = check_device(&dev);
+    if (st != LINEAR_OK) return st;
+    void* ws = scratch_address(dev);
+    if (!ws) return LINEAR_E_DEVICE;
+    return run_indexed(lin::kF16, false, x, ldx, w, ldw, sw, idx, y, ldy, E, M, N, K, ws, kNoAllocScratchBytes,
+                       stream);
+}
 
 int64_t linear_indexed_workspace_bytes(int64_t E, int64_t M) {
     if (E < 0 || M < 0 || E > kMaxGridY || M > kMaxDim) return -1;
@@ -655,6 +697,7 @@ const char* linear_status_string(int32_t status) {
         case LINEAR_E_EPILOGUE: return "invalid epilogue program: step count or step code";
         case LINEAR_E_CAPTURE: return "the first activation epilogue on a device cannot run under stream capture";
         case LINEAR_E_WORKSPACE: return "workspace not 16-byte aligned or smaller than linear_indexed_workspace_bytes";
+        case LINEAR_E_SCRATCH: return "the call needs more routing scratch than LINEAR_NOALLOC_SCRATCH_BYTES";
         default: return "unknown status";
     }
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         assert la.linear_status_string(code) != "unknown status"
     assert la.linear_status_string(99) == "unknown status"
 
@@ -242,6 +242,38 @@ def test_indexed_noops_and_device_check():
     assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_OK)
     if not torch.cuda.is_available():
         assert rc == la.LINEAR_E_DEVICE
+
+
+@needs_lib
+def test_indexed_noalloc_host_checks():
+    """The no-allocation call: the workspace call's shape checks and no-ops, and
+    LINEAR_E_SCRATCH (before any device work) when the routing would not fit the
+    library's scratch array."""
+    f = la._lib().linear_f16_indexed_noalloc
+    ws_bytes = la._lib().linear_indexed_workspace_bytes
+
+    def call(**kw):
+        a = dict(x=X, ldx=64, w=W, ldw=32, sw=64 * 32, idx=I, y=Y, ldy=32, E=4, M=48, N=32, K=64)
+        a.update(kw)
+        return f(a["x"], a["ldx"], a["w"], a["ldw"], a["sw"], a["idx"], a["y"], a["ldy"], a["E"], a["M"], a["N"],
+                 a["K"], None)
+    assert call(E=-1) == la.LINEAR_E_SHAPE and call(M=-1) == la.LINEAR_E_SHAPE and call(E=65536) == la.LINEAR_E_SHAPE
+    assert call(E=0, x=0, w=0, idx=0, y=0) == la.LINEAR_OK
+    assert call(M=0, idx=0) == la.LINEAR_OK
+    # the largest row count that fits at 8 experts, and one more
+    m = 1
+    while ws_bytes(8, 2 * m) <= la.NOALLOC_SCRATCH_BYTES:
+        m *= 2
+    lo, hi = m, 2 * m
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if ws_bytes(8, mid) <= la.NOALLOC_SCRATCH_BYTES else (lo, mid)
+    assert lo > 150000
+    assert call(E=8, M=hi, ldx=64) == la.LINEAR_E_SCRATCH
+    rc = call(E=8, M=lo)
+    assert rc in (la.LINEAR_E_DEVICE, la.LINEAR_E_ALIAS, la.LINEAR_OK)
+    if not torch.cuda.is_available():
+        assert call() == la.LINEAR_E_DEVICE
 
 
 def plan(M, N, K, path=0, x=X, w=W, ldx=None, ldw=None):

@@ -374,6 +374,7 @@ typedef struct linear_plan {
     int32_t tile_m2;    /* the second launch's tile (0 when not split) */
     int32_t tile_n2;
     int64_t grid2;      /* the second launch's workgroups (0 when not split) */
+    int32_t stages;     /* GEMM: slices of tile_k K in its LDS ring (0 for the skinny path) */
 } linear_plan;
 
 /*

@@ -74,7 +74,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32), ("vector_io", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("split_n", ctypes.c_int64), ("tile_m2", ctypes.c_int32),
-                ("tile_n2", ctypes.c_int32), ("grid2", ctypes.c_int64)]
+                ("tile_n2", ctypes.c_int32), ("grid2", ctypes.c_int64), ("stages", ctypes.c_int32)]
 
 
 class _Epilogue(ctypes.Structure):

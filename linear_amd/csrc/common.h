@@ -105,6 +105,15 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t o
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
 }
 
+// Workgroup barrier for slices handed over in LDS by direct-to-LDS loads.
+// __syncthreads() orders every earlier LDS write before the barrier, and direct
+// loads count as LDS writes, so the compiler puts a wait for all of them (vmcnt
+// 0) in front of it, including loads of later slices.  Here each wave has already
+// waited for the loads the next slice needs (an explicit vmcnt), so only its own
+// LDS reads are drained (lgkmcnt 0: a slot may be refilled after the barrier);
+// the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Eight consecutive binary16 elements starting at byte offset `off`, element e
 // replaced by zero when k0 + e >= K (element-wise loader for unaligned layouts).
 __device__ inline u32x4 load8_masked(__amdgpu_buffer_rsrc_t r, uint32_t off, int k0, int K, bool row_ok) {

@@ -166,7 +166,7 @@ gemm_kernel(LinearArgs a) {
 // win_op is 0); other activation steps read their tables from global memory.
 template <int BM, int BN, int NT, int E, int MODE>
 __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, int m0, int n0, int tid,
-                                lds_u16* win = nullptr, int win_op = 0) {
+                                lds_u16* win = nullptr, int win_op = 0, const u32x4* bias8 = nullptr) {
     constexpr int CPR = BN / 8;
     constexpr int CHT = BM * CPR / NT;               // chunks per thread
     constexpr int CH = CHT < 8 ? CHT : 8;            // chunks per pass (bounds register use)
@@ -185,7 +185,7 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
         if constexpr (MODE == kOutBias) {       // the layer's own epilogue: one bias step
             u32x4 v[CH];
 #pragma unroll
-            for (int k = 0; k < CH; ++k) v[k] = load8(a.b + cc[k], true, cc[k], a.N, ep.vec16 & 2);
+            for (int k = 0; k < CH; ++k) v[k] = bias8 ? *bias8 : load8(a.b + cc[k], true, cc[k], a.N, ep.vec16 & 2);
 #pragma unroll
             for (int k = 0; k < CH; ++k) t[k] = binop8<E, false>(t[k], v[k]);
         }
@@ -221,6 +221,121 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
 #pragma unroll
         for (int k = 0; k < CH; ++k)
             store8((uint16_t*)a.y + (int64_t)rr[k] * a.ldy + cc[k], rr[k] < a.M, cc[k], a.N, ep.vec16 & 1, t[k]);
+    }
+}
+
+// The end of a streaming tile, after its last MFMA: the accumulators acc[i][j]
+// (32 x 32 blocks of wave (wm, wn), four consecutive output columns n of one row
+// m per lane and register group) leave through the LDS the ring used (RINGB
+// bytes, free again), in row order.  FP32 mode: the sums, staged as floats in
+// row bands when the tile is larger than the ring, 16-byte row stores.  Rounded
+// modes: the rounded tile staged as 16-bit words, then epi_tile (the bias or the
+// epilogue program, 16-byte row stores), with an epilogue program's first
+// activation table window copied into LDS behind the tile.
+template <int BM, int BN, int WM, int WN, int RINGB, int E, int MODE>
+__device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* smem,
+                                            f32x16 (&acc)[BN / WN / 32][BM / WM / 32], int m0, int n0, int wave,
+                                            int lane, const u32x4* bias8 = nullptr) {
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int TILEB = BM * BN * 2;
+    const int wn = wave % WN, wm = wave / WN;
+    const int lr = lane & 31, lh = lane >> 5;
+    if constexpr (MODE == kOutF32) {
+        // the FP32 sums go out the same way, staged as floats in the freed ring
+        // (in row bands when the whole tile does not fit): row r of a band holds
+        // BN / 4 chunks of 16 bytes, chunk c at position c ^ (r % (BN / 4))
+        constexpr int CPR4 = BN / 4;
+        constexpr int PASSES = (BM * BN * 4 + RINGB - 1) / (RINGB);
+        constexpr int RPP = BM / PASSES;                   // rows per band
+        static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
+        constexpr int CHT = RPP * CPR4 / NT;
+        static_assert((RPP * CPR4) % NT == 0, "chunks must divide evenly over the threads");
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
+                        if (ml >= 0 && ml < RPP) {
+                            const f32x4 v = (f32x4){acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                                    acc[i][j][g * 4 + 3]};
+                            *(f32x4*)(smem + (ml * CPR4 + ((nl / 4) ^ (ml % CPR4))) * 16) = v;
+                        }
+                    }
+                }
+            __syncthreads();
+            const bool vec = a.vec_store && ((uintptr_t)a.y % 16 == 0);
+#pragma unroll
+            for (int k = 0; k < CHT; ++k) {
+                const int c = (int)threadIdx.x + k * NT, r = c / CPR4, c4 = c % CPR4;
+                const f32x4 v = *(const f32x4*)(smem + (r * CPR4 + (c4 ^ (r % CPR4))) * 16);
+                const int m = m0 + pass * RPP + r, n = n0 + c4 * 4;
+                if (m >= a.M) continue;
+                float* dst = (float*)a.y + (int64_t)m * a.ldy + n;
+                if (vec && n + 3 < a.N) {
+                    *(f32x4*)dst = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) dst[e] = v[e];
+                }
+            }
+        }
+        return;
+    }
+
+    if constexpr (MODE != kOutF32) {
+        // stage the rounded tile in the (now free) ring, then finish it in row order:
+        // the bias or the epilogue program, and 16-byte stores of whole row chunks
+        static_assert(BM * BN * 2 <= RINGB, "the rounded tile must fit in the ring");
+        constexpr int CPR = BN / 8;
+        __syncthreads();
+        // an epilogue program's first activation: its table window goes into LDS
+        // behind the tile (32 direct loads of 1 KB: for each sign 8192 words from
+        // kActWinBase on), landing while the tile is staged
+        int win_op = 0;
+        if constexpr (MODE == kOutEpi) {
+            for (int s = 0; s < a.epi.nsteps; ++s)
+                if (win_op == 0 && epi_op(a.epi, s) >= kEpiSilu) win_op = epi_op(a.epi, s);
+            if (win_op != 0) {
+                const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(a.epi.act + (win_op - kEpiSilu) * kActWords), (short)0, kActWords * 2, kRsrcWord3);
+                constexpr int PW = 32 / NW;
+                static_assert(32 % NW == 0, "window loads must divide evenly over the waves");
+#pragma unroll
+                for (int q = 0; q < PW; ++q) {
+                    const int j = wave * PW + q, h = j >> 4, piece = j & 15;
+                    const uint32_t word = ((uint32_t)h << 15) + kActWinBase<E> + (uint32_t)piece * 512u;
+                    lds_dma16(rt, smem + TILEB + j * 1024, word * 2u + 16u * (uint32_t)lane);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int ml = wm * TM + j * 32 + lr;
+                    uint2 u;
+                    u.x = (uint32_t)narrow<E>(acc[i][j][g * 4]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 1]) << 16);
+                    u.y = (uint32_t)narrow<E>(acc[i][j][g * 4 + 2]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 3]) << 16);
+                    const int c8 = nl / 8;
+                    *(uint2*)(smem + (ml * CPR + (c8 ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
+                }
+            }
+        if constexpr (MODE == kOutEpi) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        epi_tile<BM, BN, NT, E, MODE>(a, smem, m0, n0, threadIdx.x, (lds_u16*)(smem + TILEB), win_op, bias8);
+        return;
     }
 }
 
@@ -285,6 +400,17 @@ gemm_stream(LinearArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+
+    // The bias chunk this thread adds in the epilogue, requested now so that its
+    // latency is off the tile's tail: the epilogue gives thread t the row chunks
+    // t, t + NT, ..., all at column n0 + 8 (t % (BN / 8)) since NT is a multiple
+    // of BN / 8 (on the toy layer a bias load after the main loop cost ~1.3 us).
+    static_assert((NW * 64) % (BN / 8) == 0, "a thread's epilogue chunks must share their columns");
+    u32x4 bias8 = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (MODE == kOutBias) {
+        const int c = n0 + 8 * ((int)threadIdx.x % (BN / 8));
+        bias8 = load8(a.b + c, true, c, a.N, a.epi.vec16 & 2);
+    }
 
     // This wave's loads: groups g = wave * GPW + j; group g < BN / RPL holds weight
     // rows RPL g .., the others x rows.  Lane l fetches row l / CPR of the group,
@@ -360,7 +486,7 @@ gemm_stream(LinearArgs a) {
             for (int j = 0; j < GPW; ++j)
                 if (t + 1 < STAGES || j < DPS) LIN_ISSUE_ONE(t, j);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW + DPS) : "memory");
-        __syncthreads();
+        lds_barrier();   // slice 0 only: __syncthreads() would also wait for every later slice
 
         u32x4 af[2][FN], bf[2][FM];
 #pragma unroll
@@ -402,7 +528,7 @@ gemm_stream(LinearArgs a) {
             // outstanding; the barrier also waits for every wave's last reads of
             // slot t, which the refill below overwrites
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
-            __syncthreads();
+            lds_barrier();
             read_frags(smem + ((t + 1) % STAGES) * SLICE, 0, KS & 1);
             mfmas((KS - 1) & 1);
             constexpr int D0 = DPS < GPW ? DPS : GPW;
@@ -415,117 +541,8 @@ gemm_stream(LinearArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 #undef LIN_ISSUE_ONE
-
-    if constexpr (MODE == kOutF32) {
-        // the FP32 sums go out the same way, staged as floats in the freed ring
-        // (in row bands when the whole tile does not fit): row r of a band holds
-        // BN / 4 chunks of 16 bytes, chunk c at position c ^ (r % (BN / 4))
-        constexpr int CPR4 = BN / 4;
-        constexpr int PASSES = (BM * BN * 4 + STAGES * SLICE - 1) / (STAGES * SLICE);
-        constexpr int RPP = BM / PASSES;                   // rows per band
-        static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
-        constexpr int NT = NW * 64;
-        constexpr int CHT = RPP * CPR4 / NT;
-        static_assert((RPP * CPR4) % NT == 0, "chunks must divide evenly over the threads");
-#pragma unroll
-        for (int pass = 0; pass < PASSES; ++pass) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
-#pragma unroll
-                    for (int j = 0; j < FM; ++j) {
-                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
-                        if (ml >= 0 && ml < RPP) {
-                            const f32x4 v = (f32x4){acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
-                                                    acc[i][j][g * 4 + 3]};
-                            *(f32x4*)(smem + (ml * CPR4 + ((nl / 4) ^ (ml % CPR4))) * 16) = v;
-                        }
-                    }
-                }
-            __syncthreads();
-            const bool vec = a.vec_store && ((uintptr_t)a.y % 16 == 0);
-#pragma unroll
-            for (int k = 0; k < CHT; ++k) {
-                const int c = (int)threadIdx.x + k * NT, r = c / CPR4, c4 = c % CPR4;
-                const f32x4 v = *(const f32x4*)(smem + (r * CPR4 + (c4 ^ (r % CPR4))) * 16);
-                const int m = m0 + pass * RPP + r, n = n0 + c4 * 4;
-                if (m >= a.M) continue;
-                float* dst = (float*)a.y + (int64_t)m * a.ldy + n;
-                if (vec && n + 3 < a.N) {
-                    *(f32x4*)dst = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < a.N) dst[e] = v[e];
-                }
-            }
-        }
-        return;
-    }
-
-    if constexpr (MODE != kOutF32) {
-        // stage the rounded tile in the (now free) ring, then finish it in row order:
-        // the bias or the epilogue program, and 16-byte stores of whole row chunks
-        static_assert(BM * BN * 2 <= STAGES * SLICE, "the rounded tile must fit in the ring");
-        constexpr int CPR = BN / 8;
-        __syncthreads();
-        // an epilogue program's first activation: its table window goes into LDS
-        // behind the tile (32 direct loads of 1 KB: for each sign 8192 words from
-        // kActWinBase on), landing while the tile is staged
-        int win_op = 0;
-        if constexpr (MODE == kOutEpi) {
-            for (int s = 0; s < a.epi.nsteps; ++s)
-                if (win_op == 0 && epi_op(a.epi, s) >= kEpiSilu) win_op = epi_op(a.epi, s);
-            if (win_op != 0) {
-                const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(a.epi.act + (win_op - kEpiSilu) * kActWords), (short)0, kActWords * 2, kRsrcWord3);
-                constexpr int PW = 32 / NW;
-                static_assert(32 % NW == 0, "window loads must divide evenly over the waves");
-#pragma unroll
-                for (int q = 0; q < PW; ++q) {
-                    const int j = wave * PW + q, h = j >> 4, piece = j & 15;
-                    const uint32_t word = ((uint32_t)h << 15) + kActWinBase<E> + (uint32_t)piece * 512u;
-                    lds_dma16(rt, smem + TILEB + j * 1024, word * 2u + 16u * (uint32_t)lane);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
-#pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    const int ml = wm * TM + j * 32 + lr;
-                    uint2 u;
-                    u.x = (uint32_t)narrow<E>(acc[i][j][g * 4]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 1]) << 16);
-                    u.y = (uint32_t)narrow<E>(acc[i][j][g * 4 + 2]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 3]) << 16);
-                    const int c8 = nl / 8;
-                    *(uint2*)(smem + (ml * CPR + (c8 ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
-                }
-            }
-        if constexpr (MODE == kOutEpi) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        epi_tile<BM, BN, NW * 64, E, MODE>(a, smem, m0, n0, threadIdx.x, (lds_u16*)(smem + TILEB), win_op);
-        return;
-    }
-
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nb = n0 + wn * TN + i * 32 + g * 8 + lh * 4;
-#pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int m = m0 + wm * TM + j * 32 + lr;
-                if (m < a.M)
-                    store4<E, MODE>(a, m, nb, acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
-                                    acc[i][j][g * 4 + 3]);
-            }
-        }
+    finish_tile<BM, BN, WM, WN, STAGES * SLICE, E, MODE>(a, smem, acc, m0, n0, wave, lane,
+                                                        MODE == kOutBias ? &bias8 : nullptr);
 }
 
 // ---------------------------------------------------------------------------

@@ -238,6 +238,7 @@ int32_t plan(const Request& r, linear_plan* p, int cus) {
         p->tile_m = g.bm;
         p->tile_n = g.bn;
         p->tile_k = g.bk;
+        p->stages = g.stages;
         p->threads = g.wm * g.wn * 64;
         p->grid = ((r.M + g.bm - 1) / g.bm) * ((r.N + g.bn - 1) / g.bn);
         if (p->grid > kMaxGridX / 64) return LINEAR_E_SHAPE;

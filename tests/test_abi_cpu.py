@@ -292,8 +292,13 @@ def test_plans_for_the_workloads():
             assert p["path"] == la.PATH_SKINNY, name
         else:
             assert p["path"] == la.PATH_GEMM, name
-            assert p["grid"] >= 256 or name == "toy", (name, p)
+            assert p["grid"] >= 256, (name, p)
         assert p["vector_io"] == 1
+    # the toy runs 256 tiles of 64 x 64 through a 4-slice ring
+    p = plan(1024, 1024, 768)
+    assert (p["tile_m"], p["tile_n"], p["threads"], p["stages"], p["tile_k"], p["grid"]) == (64, 64, 256, 4, 64, 256)
+    assert plan(8192, 4096, 4096)["stages"] == 2 and plan(2000, 4000, 14336)["stages"] == 3
+    assert plan(16, 4096, 4096)["stages"] == 0                # the skinny path has no ring
 
 
 @needs_lib

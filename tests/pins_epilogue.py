@@ -376,29 +376,45 @@ def pin_special_values(orc):
             assert np.isnan(values(got, elem)).all()
 
 
-GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "epilogue_chains_bf16.txt")
+GOLDEN_DIR = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def _golden_chains(orc, name, elem):
+    """The hand-derived composition results of tests/golden/<name>: every line is
+    `op x y`, x an element-type value, y the composition with every primitive
+    rounded to the element type (derivations in the file)."""
+    ops = {"silu": oracle.EPI_SILU, "gelu_tanh": oracle.EPI_GELU_TANH, "gelu_erf": oracle.EPI_GELU_ERF}
+    n = 0
+    for line in open(__import__("os").path.join(GOLDEN_DIR, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        op, x, y = line.split()
+        w = np.array([encode(float(x), elem)], np.uint16)
+        assert round_exact(Fraction(float(x)), elem) == int(w[0]), "fixture input not of the element type"
+        assert round_exact(Fraction(float(y)), elem) == int(encode(float(y), elem)), "fixture result not of the element type"
+        got = float(values(orc.unary(ops[op], w, elem), elem)[0])
+        assert got == float(y), (op, x, got, y)
+        n += 1
+    return n
 
 
 def pin_golden_chains_bf16(orc):
     """Hand-derived bfloat16 composition results (tests/golden/epilogue_chains_bf16.txt)
     where rounding every primitive changes the answer."""
-    ops = {"silu": oracle.EPI_SILU, "gelu_tanh": oracle.EPI_GELU_TANH, "gelu_erf": oracle.EPI_GELU_ERF}
-    n = 0
-    for line in open(GOLDEN):
-        line = line.strip()
-        if not line or line.startswith("#"):
-            continue
-        op, x, y = line.split()
-        w = np.array([encode(float(x), tolerance.BF16)], np.uint16)
-        assert round_exact(Fraction(float(x)), tolerance.BF16) == int(w[0]), "fixture input not bfloat16"
-        got = float(values(orc.unary(ops[op], w, tolerance.BF16), tolerance.BF16)[0])
-        assert got == float(y), (op, x, got, y)
-        n += 1
-    assert n == 6
+    assert _golden_chains(orc, "epilogue_chains_bf16.txt", tolerance.BF16) == 6
+
+
+def pin_golden_chains_f16(orc):
+    """Hand-derived binary16 composition results (tests/golden/epilogue_chains_f16.txt)
+    where rounding every primitive changes the answer; four of them turn on a tie
+    at an intermediate step."""
+    assert _golden_chains(orc, "epilogue_chains_f16.txt", tolerance.F16) == 6
 
 
 # cheapest first: the mutation check stops at the first pin that fails
 EPILOGUE_PINS = [
+    pin_golden_chains_f16,
     pin_golden_chains_bf16,
     pin_f64_to_elem,
     pin_binary_steps_vs_exact,

@@ -80,6 +80,16 @@ EPI_MUTANTS = [
      "for (int s = nsteps - 1; s >= 0; --s)\n            v = epi_step(elem, ops[s],"),
     ("epi_round_ties_away", "r = nearbyint(a / q) * q;", "r = round(a / q) * q;"),
     ("epi_round_no_subnormal_grid", "if (e < emin) e = emin;                  /* subnormal grid */", ""),
+    # binary16-only slips that stay within the compositions' error bounds: a
+    # constant one unit off, and an intermediate left unrounded
+    ("epi_f16_c2_one_ulp_off", "const uint16_t c2 = cst(elem, -2.0 * sqrt(2.0 / 3.14159265358979323846));",
+     "const uint16_t c2 = cst(elem, -2.0 * sqrt(2.0 / 3.14159265358979323846) * (elem ? 1.0 : 1.0005));"),
+    ("epi_f16_silu_unrounded_denominator", "    return rd(elem, wd(elem, x) / wd(elem, d));\n}\n\nuint16_t oracle_epi_gelu_tanh",
+     "    return rd(elem, wd(elem, x) / (elem ? wd(elem, d) : 1.0 + wd(elem, e)));\n}\n\nuint16_t oracle_epi_gelu_tanh"),
+    ("epi_f16_gelu_erf_unrounded_sum", "uint16_t h = rd(elem, wd(elem, x) * wd(elem, g));",
+     "uint16_t h = rd(elem, wd(elem, x) * (elem ? wd(elem, g) : 1.0 + wd(elem, f)));"),
+    ("epi_f16_gelu_tanh_unrounded_inner", "uint16_t z = rd(elem, wd(elem, d) * wd(elem, c2));",
+     "uint16_t z = rd(elem, (elem ? wd(elem, d) : wd(elem, x) + wd(elem, c)) * wd(elem, c2));"),
     ("epi_round_max_overflows", "if (r > maxv) bits = elem ? 0x7f80u : 0x7c00u;", "if (r >= maxv) bits = elem ? 0x7f80u : 0x7c00u;"),
 ]
 

@@ -583,12 +583,15 @@ hipError_t launch_gemm_t(int cfg, const LinearArgs& a, int mode, hipStream_t str
 template <int E>
 hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStream_t stream) {
     switch (cfg) {
-        // the load spread measured best on the two-slot 256 x 256 tile only
+        // load spread (K steps a slice's refill is spread over), measured per tile
+        // with the ring's own barriers: 256 x 256 best at 1, 256 x 128 and 128 x 128
+        // at 2 (down 241 -> 222 us), 64 x 64 at 1; 128 x 256 (32-wide slices)
+        // has no step to spare
         case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E, 1>(mode), a, 512, stream);
-        case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E, 0>(mode), a, 512, stream);
+        case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E, 2>(mode), a, 512, stream);
         case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E, 0>(mode), a, 512, stream);
-        case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E, 0>(mode), a, 256, stream);
-        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E, 0>(mode), a, 256, stream);
+        case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E, 2>(mode), a, 256, stream);
+        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E, 1>(mode), a, 256, stream);
         default: return hipErrorInvalidValue;
     }
 }

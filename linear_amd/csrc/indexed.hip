@@ -181,11 +181,23 @@ __device__ inline int block_scan_1024(int v, int* wsum, int* total) {
     return r;
 }
 
+// Row tiles of an expert with c rows: ceil(c / BM), or, when absorbing, only its
+// f = c / BM full tiles if the r = c mod BM rows left over fit xr more into each
+// of them (0 < r <= xr f).
+__device__ inline int expert_tiles(int c, int BM, int xr, bool absorb) {
+    const int f = c / BM, r = c - f * BM;
+    return f + (r > 0 && !(absorb && f > 0 && r <= xr * f));
+}
+
 // The routing pass: tile count, row list and tile table into the workspace.
 // Row list: the rows of expert 0, then expert 1, ...; tile v = {first list
-// position, expert, rows (<= BM)}.
-__global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict__ idx, int M, int E, int BM,
-                                                      int32_t* __restrict__ ws) {
+// position, expert, rows}.  Tiles hold at most BM rows, except that when the
+// leftover rows of the experts would need another round of workgroups (tiles x
+// tiles_n over cus), an expert's leftover rows are spread over its full tiles
+// instead, up to xr more rows each, wherever they fit (tiles of BM + r / f rows,
+// the first r mod f of them one more).
+__global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict__ idx, int M, int E, int BM, int xr,
+                                                      int tiles_n, int cus, int32_t* __restrict__ ws) {
     __shared__ int cnt[kIdxMaxExperts];
     __shared__ int cur[kIdxMaxExperts];
     __shared__ int tbase[kIdxMaxExperts];
@@ -203,17 +215,24 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     __syncthreads();
 
     // prefix sums over the experts of rows and of tiles: thread t owns experts 4t .. 4t+3
-    int c[4], rs = 0, ts = 0;
+    int c[4], rs = 0, ts = 0, ta = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * tid + j;
         c[j] = e < E ? cnt[e] : 0;
         rs += c[j];
-        ts += (c[j] + BM - 1) / BM;
+        ts += expert_tiles(c[j], BM, xr, false);
+        ta += expert_tiles(c[j], BM, xr, true);
     }
+    // absorb only when it saves a round of workgroups on the CUs
+    int tplain, tabs;
+    block_scan_1024(ts, wsum, &tplain);
+    block_scan_1024(ta, wsum, &tabs);
+    const int64_t cap = (int64_t)cus;
+    const bool absorb = (tabs * (int64_t)tiles_n + cap - 1) / cap < (tplain * (int64_t)tiles_n + cap - 1) / cap;
     int rtot, ttot;
     int r0 = block_scan_1024(rs, wsum, &rtot);
-    int t0 = block_scan_1024(ts, wsum, &ttot);
+    int t0 = block_scan_1024(absorb ? ta : ts, wsum, &ttot);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * tid + j;
@@ -222,7 +241,7 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
             tbase[e] = t0;
         }
         r0 += c[j];
-        t0 += (c[j] + BM - 1) / BM;
+        t0 += expert_tiles(c[j], BM, xr, absorb);
     }
     if (tid == 0) ws[0] = ttot;
     __syncthreads();
@@ -235,8 +254,14 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
             if (tbase[mid] <= v) lo = mid;
             else hi = mid - 1;
         }
-        const int t = v - tbase[lo];
-        tiles[v] = make_int4(cur[lo] + t * BM, lo, min(BM, cnt[lo] - t * BM), 0);
+        const int t = v - tbase[lo], ce = cnt[lo];
+        const int f = ce / BM, r = ce - f * BM;
+        if (absorb && f > 0 && r > 0 && r <= xr * f) {
+            const int q = r / f, rm = r - q * f;
+            tiles[v] = make_int4(cur[lo] + t * (BM + q) + min(t, rm), lo, BM + q + (t < rm ? 1 : 0), 0);
+        } else {
+            tiles[v] = make_int4(cur[lo] + t * BM, lo, min(BM, ce - t * BM), 0);
+        }
     }
     __syncthreads();
 
@@ -247,14 +272,52 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     }
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// LDS byte address of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-// The transposing LDS read at byte offset off of the workgroup's LDS.
-__device__ inline uint2 lds_read_tr16(const unsigned char* base, uint32_t off) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)((__attribute__((address_space(3))) unsigned char*)base + off));
-    return __builtin_bit_cast(uint2, v);
+// The transposing LDS read (ds_read_b64_tr_b16) at LDS byte address addr + OFF,
+// as inline assembly.  The compiler cannot tell which LDS bytes the builtin form
+// reads, so before each one it makes the wave wait for every direct-to-LDS load
+// in flight (vmcnt 0), the loads of the slices ahead included: a ring would then
+// never overlap its loads with the MFMAs.  The wait insertion does not look into
+// inline assembly, so the caller waits for the result itself (lds_ready) before
+// any use; LDS operations of a wave complete in issue order.
+template <int OFF>
+__device__ __forceinline__ uint2 lds_tr16(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "the ds offset field is 16 bits");
+    uint2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+
+// The same read of 16 bytes (ds_read_b128) for operands whose wait goes with the
+// transposing reads around them.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "the ds offset field is 16 bits");
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+
+// Wait until at most N of the wave's LDS operations are outstanding, with the
+// registers of a and b as operands, so that no use of them moves above the wait.
+template <int N, typename A>
+__device__ __forceinline__ void lds_ready(A& a) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N, typename A, typename B>
+__device__ __forceinline__ void lds_ready(A& a, B& b) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N, typename A, typename B, typename C>
+__device__ __forceinline__ void lds_ready(A& a, B& b, C& c) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
 }
 
 // Swizzle of the panel rows: the 32-byte column pair u of k-row kr sits at pair
@@ -271,12 +334,17 @@ __host__ __device__ constexpr int pair_swz(int kr) { return 2 * (kr & 3) | ((kr 
 // as (TN / 32) x (TM / 32) blocks of v_mfma_f32_32x32x16 (panel columns as the
 // A operand, x rows as B).
 //
+// A tile may hold up to XR rows more than BM (the routing pass's absorbed
+// leftover rows): rows BM .. BM + XR - 1 form one more 32-row block, of which
+// wave (wm, wn) multiplies the 32 columns wn TN + 32 wm against the same panel
+// fragments.
+//
 // LDS slot of one 64-k slice: the panel, 64 k-rows of BN columns (2 BN bytes,
-// pair-swizzled as above), then BM x rows of 64 k (128 bytes, 16-byte chunk c
-// of row r at c ^ ((r >> 1) & 7), as in the dense kernel).  Each direct load
-// fills 1 KB of the slot; lane l lands at byte 16 l of it and fetches the chunk
-// that the swizzle places there.
-template <int BM, int BN, int WM, int WN, int STAGES, int E, int MODE>
+// pair-swizzled as above), then XS >= BM + XR x rows of 64 k (128 bytes, 16-byte
+// chunk c of row r at c ^ ((r >> 1) & 7), as in the dense kernel; rows past the
+// tile's load as zero).  Each direct load fills 1 KB of the slot; lane l lands
+// at byte 16 l of it and fetches the chunk that the swizzle places there.
+template <int BM, int BN, int WM, int WN, int STAGES, int XR, int E, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 indexed_routed(IndexedArgs a) {
     constexpr int BK = 64, KS = BK / 16;
@@ -285,7 +353,8 @@ indexed_routed(IndexedArgs a) {
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int PROW = 2 * BN;                      // bytes per panel k-row
     constexpr int PBYTES = BK * PROW;
-    constexpr int XBYTES = BM * BK * 2;
+    constexpr int XS = (BM + XR + 8 * NW - 1) / (8 * NW) * (8 * NW);   // x rows per slot: whole loads per wave
+    constexpr int XBYTES = XS * BK * 2;
     constexpr int SLICE = PBYTES + XBYTES;
     constexpr int GP = PBYTES / 1024, GX = XBYTES / 1024;
     constexpr int GPP = GP / NW, GPX = GX / NW;       // panel and x loads per wave per slice
@@ -294,6 +363,7 @@ indexed_routed(IndexedArgs a) {
     static_assert(BM % 32 == 0 && TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(GP % NW == 0 && GX % NW == 0, "direct loads must divide evenly over the waves");
     static_assert(STAGES >= 2 && STAGES * SLICE <= 160 * 1024, "LDS ring too large");
+    static_assert(XR == 0 || (XR == 32 && FN == WM), "one extra 32-row block, a column block per wave row");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
 
     const int tiles_n = (a.N + BN - 1) / BN;
@@ -356,15 +426,16 @@ indexed_routed(IndexedArgs a) {
         const int n = wn * TN + i * 32 + 16 * (q & 1) + 4 * (s & 3);
         aoff[i] = kq * PROW + (((n >> 3) ^ (2 * sw)) << 4) + 8 * ((n >> 2) & 1);
     }
+    // x fragment j of K step ks: row r = wm TM + 32 j + lr at r * 128 within the x
+    // part, chunk (2 ks + lh) ^ ((r >> 1) & 7); 32 j + wm TM is a multiple of 16, so
+    // the chunk does not depend on j and 32 j rows go into the constant offset
+    static_assert(TM % 16 == 0, "x fragment rows keep their swizzle across blocks");
     const int lr = lane & 31, lh = lane >> 5;
-    uint32_t boff[KS][FM];
+    uint32_t boff[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int r = wm * TM + j * 32 + lr;
-            boff[ks][j] = PBYTES + r * 128 + (((ks * 2 + lh) ^ ((r >> 1) & 7)) << 4);
-        }
+    for (int ks = 0; ks < KS; ++ks) boff[ks] = (wm * TM + lr) * 128 + (((ks * 2 + lh) ^ ((lr >> 1) & 7)) << 4);
+    // the extra block's x fragment: row BM + lr, at boff + xdelta
+    const uint32_t xdelta = (uint32_t)((BM - wm * TM) * 128);
 
 #define LIN_IDX_ISSUE(t_, j_)                                                                    \
     do {                                                                                         \
@@ -383,6 +454,7 @@ indexed_routed(IndexedArgs a) {
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
+    f32x16 accx = (f32x16){};                         // the extra rows' block (XR > 0)
 
     if (nk > 0) {
         // as in the dense streaming kernel: loads past the last slice carry
@@ -397,52 +469,71 @@ indexed_routed(IndexedArgs a) {
         // The wave's work scales with the tile's rows: FA of its FM row blocks
         // hold rows, and the reads and MFMAs of the others are skipped (one copy
         // of the pipeline per FA; every copy issues the same loads and barriers).
-        auto pipeline = [&]<int FA>() {
-            u32x4 af[2][FN], bf[2][FM];
-            auto read_frags = [&](const unsigned char* slot, int ks, int buf) {
+        // Fragment reads are inline assembly (lds_tr16, lds_b128): the reads of
+        // one K step go into buffer BUF while the MFMAs of the other buffer run,
+        // and the MFMAs of BUF first wait until only the reads of the following
+        // step (2 FN + FA + XA) are outstanding.  XA: the tile has extra rows.
+        auto pipeline = [&]<int FA, bool XA>() {
+            constexpr int NR = 2 * FN + FA + (XA ? 1 : 0);   // reads per K step
+            uint2 alo[2][FN], ahi[2][FN];
+            u32x4 bf[2][FM], bx[2];
+            auto read_frags = [&]<int KS_, int BUF>(uint32_t slot) {
                 if constexpr (FA > 0) {
-#pragma unroll
-                    for (int i = 0; i < FN; ++i) {
-                        const uint2 lo = lds_read_tr16(slot, aoff[i] + (16 * ks) * PROW);
-                        const uint2 hi = lds_read_tr16(slot, aoff[i] + (16 * ks + 4) * PROW);
-                        af[buf][i] = (u32x4){lo.x, lo.y, hi.x, hi.y};
-                    }
-#pragma unroll
-                    for (int j = 0; j < FA; ++j) bf[buf][j] = *(const u32x4*)(slot + boff[ks][j]);
+                    static_for<0, FN>([&]<int i>() {
+                        alo[BUF][i] = lds_tr16<(16 * KS_) * PROW>(slot + aoff[i]);
+                        ahi[BUF][i] = lds_tr16<(16 * KS_ + 4) * PROW>(slot + aoff[i]);
+                    });
+                    static_for<0, FA>([&]<int j>() { bf[BUF][j] = lds_b128<PBYTES + 32 * 128 * j>(slot + boff[KS_]); });
+                    if constexpr (XA) bx[BUF] = lds_b128<PBYTES>(slot + boff[KS_] + xdelta);
                 }
             };
-            auto mfmas = [&](int buf) {
+            auto mfmas = [&]<int BUF>() {
+                if constexpr (FA > 0) {
+                    static_for<0, FN>([&]<int i>() { lds_ready<NR>(alo[BUF][i], ahi[BUF][i]); });
+                    static_for<0, FA>([&]<int j>() { lds_ready<NR>(bf[BUF][j]); });
+                    u32x4 af[FN];
 #pragma unroll
-                for (int i = 0; i < FN; ++i)
+                    for (int i = 0; i < FN; ++i) {
+                        af[i] = (u32x4){alo[BUF][i].x, alo[BUF][i].y, ahi[BUF][i].x, ahi[BUF][i].y};
 #pragma unroll
-                    for (int j = 0; j < FA; ++j)
-                        acc[i][j] = mfma32x32x16<E>(af[buf][i], bf[buf][j], acc[i][j]);
+                        for (int j = 0; j < FA; ++j) acc[i][j] = mfma32x32x16<E>(af[i], bf[BUF][j], acc[i][j]);
+                    }
+                    if constexpr (XA) {
+                        lds_ready<NR>(bx[BUF]);
+                        accx = mfma32x32x16<E>(wm ? af[1] : af[0], bx[BUF], accx);
+                    }
+                }
             };
-            read_frags(smem, 0, 0);
+            const uint32_t base = lds_addr(smem);
+            read_frags.template operator()<0, 0>(base);
 
             for (int t = 0; t < nk; ++t) {
                 // slice t + STAGES - 1 goes into the slot released by the barrier
                 // that ended slice t - 1
 #pragma unroll
                 for (int j = 0; j < GPW; ++j) LIN_IDX_ISSUE(t + STAGES - 1, j);
-                const unsigned char* slot = smem + (t % STAGES) * SLICE;
+                const uint32_t slot = base + (t % STAGES) * SLICE;
                 static_for<0, KS - 1>([&]<int ks>() {
-                    read_frags(slot, ks + 1, (ks + 1) & 1);
-                    mfmas(ks & 1);
-                    if constexpr (FA > 0) order_step<FN * FA, 2 * FN + FA, 0>();
+                    read_frags.template operator()<ks + 1, (ks + 1) & 1>(slot);
+                    mfmas.template operator()<ks & 1>();
+                    __builtin_amdgcn_sched_barrier(0);
                 });
                 // slice t + 1 has landed once only the later slices' loads are
-                // outstanding; the barrier also waits for every wave's reads of slot t
+                // outstanding; the barrier also drains every wave's reads of slot t
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
-                __syncthreads();
-                if (t + 1 < nk) read_frags(smem + ((t + 1) % STAGES) * SLICE, 0, KS & 1);
-                mfmas((KS - 1) & 1);
+                lds_barrier();
+                if (t + 1 < nk) read_frags.template operator()<0, KS & 1>(base + ((t + 1) % STAGES) * SLICE);
+                mfmas.template operator()<(KS - 1) & 1>();
             }
         };
         const int active = min(FM, max(0, (rows - wm * TM + 31) / 32));   // uniform
-        static_for<0, FM + 1>([&]<int fa>() {
-            if (active == fa) pipeline.template operator()<fa>();
-        });
+        if (XR > 0 && rows > BM) {
+            if constexpr (XR > 0) pipeline.template operator()<FM, true>();
+        } else {
+            static_for<0, FM + 1>([&]<int fa>() {
+                if (active == fa) pipeline.template operator()<fa, false>();
+            });
+        }
         // the zero-fill loads past the end must land before the LDS is released
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -453,7 +544,8 @@ indexed_routed(IndexedArgs a) {
     // column wn TN + 32 i + 8 b + 4 (lane / 32) + r of tile row wm TM + 32 j +
     // lane % 32) with 16-byte chunk c of a staged row at c ^ (row mod chunks per
     // row), then every thread stores whole 16-byte chunks of the gathered rows.
-    // FP32 sums, twice the bytes of the ring, go out in two bands of rows.
+    // FP32 sums, twice the bytes of the ring, go out in two bands of rows; the
+    // extra rows of an absorbing tile in a band of their own.
     {
         constexpr int NT = NW * 64;
         constexpr int EB = MODE == kOutF32 ? 4 : 2;            // output bytes per element
@@ -461,39 +553,26 @@ indexed_routed(IndexedArgs a) {
         constexpr int CPR = BN / EPC;                         // chunks per tile row
         constexpr int PASSES = (BM * BN * EB + STAGES * SLICE - 1) / (STAGES * SLICE);
         constexpr int RPP = BM / PASSES;                      // tile rows per band
-        constexpr int CHT = RPP * CPR / NT;                   // chunks per thread and band
         static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
-        static_assert((RPP * CPR) % NT == 0, "chunks must divide evenly over the threads");
+        static_assert((RPP * CPR) % NT == 0 && (32 * CPR) % NT == 0, "chunks must divide evenly over the threads");
         const bool vec = a.vec_store && ((uintptr_t)a.y % 16 == 0) && (a.ldy % EPC == 0);
+        // accumulator v (4 consecutive columns from nl) into staged row ml
+        auto stage = [&](int ml, int nl, const f32x4& v) {
+            if constexpr (MODE == kOutF32) {
+                *(f32x4*)(smem + (ml * CPR + ((nl / 4) ^ (ml % CPR))) * 16) = v;
+            } else {
+                uint2 u;
+                u.x = (uint32_t)narrow<E>(v[0]) | ((uint32_t)narrow<E>(v[1]) << 16);
+                u.y = (uint32_t)narrow<E>(v[2]) | ((uint32_t)narrow<E>(v[3]) << 16);
+                *(uint2*)(smem + (ml * CPR + ((nl / 8) ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
+            }
+        };
+        // the staged band of RB rows, tile rows row0 .. row0 + RB - 1, to y
+        auto store_band = [&]<int RB>(int row0) {
 #pragma unroll
-        for (int pass = 0; pass < PASSES; ++pass) {
-            __syncthreads();                                  // the ring, or the last band, is free
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int nl = wn * TN + i * 32 + 8 * b + 4 * lh;
-#pragma unroll
-                    for (int j = 0; j < FM; ++j) {
-                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
-                        if (ml < 0 || ml >= RPP) continue;
-                        const f32x4 v = (f32x4){acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
-                                                acc[i][j][4 * b + 3]};
-                        if constexpr (MODE == kOutF32) {
-                            *(f32x4*)(smem + (ml * CPR + ((nl / 4) ^ (ml % CPR))) * 16) = v;
-                        } else {
-                            uint2 u;
-                            u.x = (uint32_t)narrow<E>(v[0]) | ((uint32_t)narrow<E>(v[1]) << 16);
-                            u.y = (uint32_t)narrow<E>(v[2]) | ((uint32_t)narrow<E>(v[3]) << 16);
-                            *(uint2*)(smem + (ml * CPR + ((nl / 8) ^ (ml % CPR))) * 16 + ((nl / 4) & 1) * 8) = u;
-                        }
-                    }
-                }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < CHT; ++k) {
+            for (int k = 0; k < RB * CPR / NT; ++k) {
                 const int c = (int)threadIdx.x + k * NT, r = c / CPR, cc = c % CPR;
-                const int tr = pass * RPP + r, n = n0 + cc * EPC;
+                const int tr = row0 + r, n = n0 + cc * EPC;
                 if (tr >= rows || n >= a.N) continue;
                 const u32x4 v = *(const u32x4*)(smem + (r * CPR + (cc ^ (r % CPR))) * 16);
                 const int64_t m = list[tr];
@@ -509,6 +588,36 @@ indexed_routed(IndexedArgs a) {
                     for (int e = 0; e < 8; ++e)
                         if (n + e < a.N) ((uint16_t*)dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
                 }
+            }
+        };
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            __syncthreads();                                  // the ring, or the last band, is free
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int nl = wn * TN + i * 32 + 8 * b + 4 * lh;
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
+                        if (ml < 0 || ml >= RPP) continue;
+                        stage(ml, nl, (f32x4){acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
+                                              acc[i][j][4 * b + 3]});
+                    }
+                }
+            __syncthreads();
+            store_band.template operator()<RPP>(pass * RPP);
+        }
+        if constexpr (XR > 0) {
+            if (rows > BM) {                                  // uniform
+                __syncthreads();
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    stage(lr, wn * TN + wm * 32 + 8 * b + 4 * lh,
+                          (f32x4){accx[4 * b], accx[4 * b + 1], accx[4 * b + 2], accx[4 * b + 3]});
+                __syncthreads();
+                store_band.template operator()<32>(BM);
             }
         }
     }
@@ -686,25 +795,32 @@ indexed_decode(IndexedArgs a) {
     uint32_t aoff[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) aoff[b] = abase + ((2 * (b ^ psw) + ((s & 3) >> 1)) << 4);
-    // x read (B operand): row s, chunk q
-    const uint32_t boff = PB + s * 64 + ((q ^ ((s >> 2) & 3)) << 4);
+    // x read (B operand): row s, chunk q, at PB + boff
+    const uint32_t boff = s * 64 + ((q ^ ((s >> 2) & 3)) << 4);
 
     f32x4 acc[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[b] = (f32x4){};
     for (int i = 0; i < S - 1; ++i) issue(i);
+    const uint32_t rbase = lds_addr(ring);
     for (int i = 0; i < mine; ++i) {
-        // slot (i - 1) % S: this wave's reads of it finished before its MFMAs
+        // slot (i - 1) % S: this wave's reads of it finished before its last MFMA
         issue(i + S - 1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * L) : "memory");
-        const unsigned char* slot = ring + (i % S) * WSLOT;
-        const u32x4 xb = *(const u32x4*)(slot + boff);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint2 lo = lds_read_tr16(slot, aoff[b]);
-            const uint2 hi = lds_read_tr16(slot, aoff[b] + 4 * 256);
-            acc[b] = mfma16x16x32<E>((u32x4){lo.x, lo.y, hi.x, hi.y}, xb, acc[b]);
-        }
+        const uint32_t slot = rbase + (i % S) * WSLOT;
+        // all 17 reads of the slice at once (inline assembly, see lds_tr16), then
+        // each MFMA waits for its own: 2 (7 - b) reads follow block b's
+        u32x4 xb = lds_b128<PB>(slot + boff);
+        uint2 lo[8], hi[8];
+        static_for<0, 8>([&]<int b>() {
+            lo[b] = lds_tr16<0>(slot + aoff[b]);
+            hi[b] = lds_tr16<4 * 256>(slot + aoff[b]);
+        });
+        static_for<0, 8>([&]<int b>() {
+            if constexpr (b == 0) lds_ready<14>(xb, lo[0], hi[0]);
+            else lds_ready<14 - 2 * b>(lo[b], hi[b]);
+            acc[b] = mfma16x16x32<E>((u32x4){lo[b].x, lo[b].y, hi[b].x, hi[b].y}, xb, acc[b]);
+        });
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -737,14 +853,16 @@ static const void* routed_fn(int cfg, int mode) {
     if (cfg == 2)
         return mode == kOutF32 ? (const void*)indexed_decode<4, E, kOutF32, true>
                                : (const void*)indexed_decode<4, E, kOutRound, true>;
-    return mode == kOutF32 ? (const void*)indexed_routed<256, 256, 2, 4, 2, E, kOutF32>
-                           : (const void*)indexed_routed<256, 256, 2, 4, 2, E, kOutRound>;
+    return mode == kOutF32 ? (const void*)indexed_routed<256, 256, 2, 4, 2, kIdxExtraRows, E, kOutF32>
+                           : (const void*)indexed_routed<256, 256, 2, 4, 2, kIdxExtraRows, E, kOutRound>;
 }
 
 hipError_t launch_indexed_routed(int elem, int cfg, const IndexedArgs& a, int mode, hipStream_t stream) {
     const GemmConfig& g = kIdxConfigs[cfg];
     if (cfg != 2) {
-        hipLaunchKernelGGL(indexed_route, dim3(1), dim3(1024), 0, stream, a.idx, a.M, a.E, g.bm, a.ws);
+        const int tiles_n = (int)((a.N + g.bn - 1) / g.bn);
+        hipLaunchKernelGGL(indexed_route, dim3(1), dim3(1024), 0, stream, a.idx, a.M, a.E, g.bm,
+                           cfg == 1 ? kIdxExtraRows : 0, tiles_n, a.cus, a.ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -62,6 +62,7 @@ struct IndexedArgs {
     int vec_x;              // x rows load as 16-byte fragments
     int vec_store;          // y takes 4-element vector stores
     int slots;              // routed path: row-tile slots in the grid (>= tiles used)
+    int cus;                // compute units of the device (the routing pass's round size)
 };
 
 // Row-scan kernel (any layout): one workgroup per (expert, kIdxCols columns).
@@ -92,6 +93,9 @@ inline constexpr GemmConfig kIdxConfigs[kNumIdxConfigs] = {
     {16, 128, 1, 4, 4, 32},
 };
 constexpr int kIdxSelfRouteRows = 4096;
+// Rows past 256 that a prefill tile can take in (the routing pass's absorbed
+// leftover rows of an expert).
+constexpr int kIdxExtraRows = 32;
 hipError_t launch_indexed(int elem, const IndexedArgs& a, int mode, hipStream_t stream);
 hipError_t launch_indexed_routed(int elem, int cfg, const IndexedArgs& a, int mode, hipStream_t stream);
 

@@ -469,6 +469,7 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     a.vec_x = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0) ? 1 : 0;
     a.vec_store = ((uintptr_t)y % (f32_out ? 16 : 8) == 0) && (ldy % 4 == 0) ? 1 : 0;
     a.slots = 0;
+    a.cus = di.cus;
     const int mode = f32_out ? lin::kOutF32 : lin::kOutRound;
     hipError_t e;
     if (indexed_routed_ok(x, ldx, w, ldw, sw, E, M, N, K)) {

@@ -118,3 +118,34 @@ def test_every_streaming_tile_every_output(orc, M, N, K, tile, split):
     if split:
         assert (p["tile_m2"], p["tile_n2"]) == (256, 128), p
     full_check(orc, x, w, b, la.PATH_AUTO)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+def test_moe_prefill_every_output(orc, dtype):
+    """The indexed prefill (4096 rows over 8 experts of [4096, 4096], routed at
+    random as the benchmark's inputs are) over every output: the rule of
+    oracle/tolerance.py against the oracle's projection and band ("The Graph IR",
+    op table, IndexedMatMul row).  On a 256-CU part the routing pass spreads the
+    leftover rows of some experts over their full tiles here (16 row tiles rather
+    than 19), so the extra-row blocks are among the outputs checked."""
+    elem = tolerance.BF16 if dtype == torch.bfloat16 else tolerance.F16
+    wl = workloads.INDEXED["moe_prefill"]
+    x, w, idx = workloads.make_indexed_inputs(wl.E, wl.M, wl.N, wl.K, wl.a, seed=0, dtype=dtype)
+    ws = torch.zeros(la.indexed_workspace_bytes(wl.E, wl.M), dtype=torch.uint8, device=DEV)
+    fn = la.linear_bf16_indexed if dtype == torch.bfloat16 else la.linear_f16_indexed
+    y = fn(x.to(DEV), w.to(DEV), idx.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    yw = words(y)
+    ntiles = int(ws.view(torch.int32)[0].item())
+    del y, ws
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    y_ref, _ = orc.indexed(x, w, idx.numpy(), elem=elem)
+    S, A = orc.indexed_band(x, w, idx.numpy(), elem=elem)
+    t_orc = time.perf_counter() - t0
+    ok, rep = tolerance.check_proj(yw, y_ref, A, elem=elem)
+    print("every-output parity", {"case": "moe_prefill", "dtype": str(dtype), "row_tiles": ntiles,
+                                  "outputs": int(yw.size), "rule_failures": int((~ok).sum()),
+                                  "max_ulp": round(rep["max_ulp"], 3), "oracle_s": round(t_orc, 2)}, flush=True)
+    assert ok.all(), rep
+    assert tolerance.in_outer_band(yw, S, A, wl.K, elem=elem).all()

@@ -284,6 +284,81 @@ def test_indexed_routed_misaligned_output_with_guard_band(orc, M, E, N, K, f32, 
         assert (gw[band] == three).all()
 
 
+# Rows of each expert, with the row tiles the routing pass cuts them into when it
+# spreads leftover rows over an expert's full tiles (up to 32 more rows each) and
+# when it does not: (rows, tiles absorbing, tiles plain).
+ABSORB_COUNTS = [
+    (532, 2, 3),     # 512 + 20: two tiles of 266 rows
+    (576, 2, 3),     # 512 + 64: two tiles of 288, the most a tile takes
+    (288, 1, 2),     # 256 + 32: one tile of 288
+    (289, 2, 2),     # 256 + 33: one row too many, kept as a tile of 33
+    (496, 2, 2),     # 256 + 240
+    (800, 3, 4),     # 768 + 32: tiles of 267, 267 and 266 rows
+    (100, 1, 1),     # no full tile
+    (0, 0, 0),       # an expert without rows
+]
+# The routed workspace: a 64-word header (word 0: the tile count), the M-word row
+# list, then the tile table of {first list position, expert, rows, 0} from the
+# next multiple of 4 words.
+WS_HEADER_WORDS = 64
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("N", [4096, 520], ids=["absorbing", "plain"])
+def test_indexed_absorbed_rows_bit_exact(orc, N, dtype):
+    """Experts whose leftover rows the routing pass spreads over their full tiles
+    (tiles of up to 288 rows: the extra 32-row block of the 256-row kernel) when
+    that saves a round of workgroups on the CUs (N = 4096: 16 column tiles), and
+    the same rows in tiles of at most 256 when it does not (N = 520): every output
+    bit for bit on integer data, rounded and FP32 sums, rows without an expert
+    untouched, and the tile table read back from the caller's workspace."""
+    elem = elem_of(dtype)
+    E, K = len(ABSORB_COUNTS), 72
+    g = torch.Generator().manual_seed(N)
+    idx = torch.cat([torch.full((c,), e) for e, (c, _, _) in enumerate(ABSORB_COUNTS)] + [torch.full((37,), -1)])
+    idx = idx[torch.randperm(idx.numel(), generator=g)].to(torch.int32)
+    M = idx.numel()
+    r = 30 if dtype == F16 else 6
+    x, w = ints((M, K), r, M + K, dtype), ints((E, K, N), r, E + N, dtype)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_n = (N + 255) // 256
+
+    def rounds(t):
+        return (t * tiles_n + cus - 1) // cus
+
+    t_abs = sum(a for _, a, _ in ABSORB_COUNTS)
+    t_plain = sum(p for _, _, p in ABSORB_COUNTS)
+    absorb = rounds(t_abs) < rounds(t_plain)
+    if N == 4096 and cus == 256:
+        assert absorb, "13 tiles fit one round of 256 workgroups, 17 do not"
+    ws = torch.zeros(la.indexed_workspace_bytes(E, M), dtype=torch.uint8, device=DEV)
+    sentinel = torch.full((M, N), 5.0, dtype=dtype)
+    fn = la.linear_bf16_indexed if dtype == BF else la.linear_f16_indexed
+    y = fn(x.to(DEV), w.to(DEV), idx.to(DEV), out=sentinel.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    table = ws.view(torch.int32).cpu().numpy()
+    ntiles = int(table[0])
+    assert ntiles == (t_abs if absorb else t_plain), (ntiles, absorb)
+    t0 = (WS_HEADER_WORDS + M + 3) & ~3
+    tiles = table[t0:t0 + 4 * ntiles].reshape(ntiles, 4)
+    per_expert = [sorted(tiles[tiles[:, 1] == e, 2].tolist()) for e in range(E)]
+    for e, (c, _, _) in enumerate(ABSORB_COUNTS):
+        assert sum(per_expert[e]) == c, (e, per_expert[e])
+    assert max(tiles[:, 2]) == (288 if absorb else 256)
+    if absorb:
+        assert per_expert[5] == [266, 267, 267] and per_expert[3] == [33, 256]
+    y_ref, s_ref = orc.indexed(x, w, idx.numpy(), elem=elem, y_init=words(sentinel))
+    ok = eq_words(words(y), y_ref, elem)
+    assert ok.all(), (~ok).sum()
+    s = (la.linear_bf16_indexed_f32out if dtype == BF else la.linear_f16_indexed_f32out)(
+        x.to(DEV), w.to(DEV), idx.to(DEV), out=torch.zeros(M, N, device=DEV), workspace=ws)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    valid = (idx.numpy() >= 0) & (idx.numpy() < E)
+    assert np.array_equal(s[valid].view(np.uint32), s_ref[valid].view(np.uint32))
+    assert (s[~valid] == 0).all()
+
+
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 def test_indexed_reused_workspace(orc, dtype):
     """One caller-owned workspace through calls of different sizes and both row

@@ -151,32 +151,49 @@ indexed_kernel(IndexedArgs a) {
 // ---------------------------------------------------------------------------
 // Routed path
 
-// Exclusive prefix sum of v over the 1024 threads; *total gets the sum.  Uses
-// wsum (16 words) and ends with a barrier.
-__device__ inline int block_scan_1024(int v, int* wsum, int* total) {
+// Exclusive prefix sums of a and b over the 1024 threads (both in the same
+// shuffles and barriers); *ta and *tb get the sums.  Uses wsum (66 words) and
+// ends with a barrier.
+__device__ inline int2 block_scan2_1024(int a, int b, int* wsum, int* ta, int* tb) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
+    int ia = a, ib = b;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
+        const int xa = __shfl_up(ia, o, 64), xb = __shfl_up(ib, o, 64);
+        if (lane >= o) {
+            ia += xa;
+            ib += xb;
+        }
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) {
+        wsum[wave] = ia;
+        wsum[16 + wave] = ib;
+    }
     __syncthreads();
     if (wave == 0) {
-        const int s = lane < 16 ? wsum[lane] : 0;
-        int si = s;
+        const int sa = lane < 16 ? wsum[lane] : 0, sb = lane < 16 ? wsum[16 + lane] : 0;
+        int ja = sa, jb = sb;
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-            const int t = __shfl_up(si, o, 64);
-            if (lane >= o) si += t;
+            const int xa = __shfl_up(ja, o, 64), xb = __shfl_up(jb, o, 64);
+            if (lane >= o) {
+                ja += xa;
+                jb += xb;
+            }
         }
-        if (lane < 16) wsum[16 + lane] = si - s;   // exclusive wave offsets
-        if (lane == 15) wsum[32] = si;
+        if (lane < 16) {
+            wsum[32 + lane] = ja - sa;                // exclusive wave offsets
+            wsum[48 + lane] = jb - sb;
+        }
+        if (lane == 15) {
+            wsum[64] = ja;
+            wsum[65] = jb;
+        }
     }
     __syncthreads();
-    const int r = wsum[16 + wave] + incl - v;
-    *total = wsum[32];
+    const int2 r = make_int2(wsum[32 + wave] + ia - a, wsum[48 + wave] + ib - b);
+    *ta = wsum[64];
+    *tb = wsum[65];
     __syncthreads();
     return r;
 }
@@ -201,16 +218,26 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     __shared__ int cnt[kIdxMaxExperts];
     __shared__ int cur[kIdxMaxExperts];
     __shared__ int tbase[kIdxMaxExperts];
-    __shared__ int wsum[48];
+    __shared__ int wsum[66];
     const int tid = threadIdx.x;
     int32_t* perm = ws + kIdxHeaderWords;
     int4* tiles = (int4*)(ws + idx_ws_tiles(M));
 
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
-    for (int m = tid; m < M; m += 1024) {
-        const int e = idx[m];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    if (tid == 0) wsum[64] = wsum[65] = 0;
+    // idx is read 4 rows per thread at a time, the loads issued together
+    for (int m0 = 0; m0 < M; m0 += 4096) {
+        int e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + 1024 * j + tid;
+            const int v = idx[min(m, M - 1)];         // unconditional: the four loads go out together
+            e[j] = m < M ? v : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((unsigned)e[j] < (unsigned)E) atomicAdd(&cnt[e[j]], 1);
     }
     __syncthreads();
 
@@ -225,14 +252,15 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
         ta += expert_tiles(c[j], BM, xr, true);
     }
     // absorb only when it saves a round of workgroups on the CUs
-    int tplain, tabs;
-    block_scan_1024(ts, wsum, &tplain);
-    block_scan_1024(ta, wsum, &tabs);
+    if (ts) atomicAdd(&wsum[64], ts);
+    if (ta) atomicAdd(&wsum[65], ta);
+    __syncthreads();
+    const int tplain = wsum[64], tabs = wsum[65];
     const int64_t cap = (int64_t)cus;
     const bool absorb = (tabs * (int64_t)tiles_n + cap - 1) / cap < (tplain * (int64_t)tiles_n + cap - 1) / cap;
     int rtot, ttot;
-    int r0 = block_scan_1024(rs, wsum, &rtot);
-    int t0 = block_scan_1024(absorb ? ta : ts, wsum, &ttot);
+    const int2 st = block_scan2_1024(rs, absorb ? ta : ts, wsum, &rtot, &ttot);
+    int r0 = st.x, t0 = st.y;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * tid + j;
@@ -266,9 +294,17 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     __syncthreads();
 
     // row list: each row takes the next free slot of its expert
-    for (int m = tid; m < M; m += 1024) {
-        const int e = idx[m];
-        if ((unsigned)e < (unsigned)E) perm[atomicAdd(&cur[e], 1)] = m;
+    for (int m0 = 0; m0 < M; m0 += 4096) {
+        int e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + 1024 * j + tid;
+            const int v = idx[min(m, M - 1)];
+            e[j] = m < M ? v : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((unsigned)e[j] < (unsigned)E) perm[atomicAdd(&cur[e[j]], 1)] = m0 + 1024 * j + tid;
     }
 }
 

@@ -7,7 +7,9 @@
 //
 // Routed (16-byte aligned layouts).  A routing pass (one workgroup) counts the
 // rows of each expert, lays out the row list expert by expert and cuts it into
-// row tiles of at most BM rows: the tile table.  The contraction kernel then runs
+// row tiles of at most BM rows (the 256-row tiles take up to 32 leftover rows of
+// their expert when that saves a round of workgroups): the tile table.  The
+// contraction kernel then runs
 // one workgroup per (tile, BN output columns), a GEMM over the tile's gathered x
 // rows and the expert's [K, BN] column panel, streamed through an LDS ring by
 // direct-to-LDS loads, 64 k per slice.  The table is k-major ([K, N], n

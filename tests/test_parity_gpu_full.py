@@ -141,11 +141,18 @@ def test_moe_prefill_every_output(orc, dtype):
     torch.cuda.empty_cache()
     t0 = time.perf_counter()
     y_ref, _ = orc.indexed(x, w, idx.numpy(), elem=elem)
-    S, A = orc.indexed_band(x, w, idx.numpy(), elem=elem)
     t_orc = time.perf_counter() - t0
-    ok, rep = tolerance.check_proj(yw, y_ref, A, elem=elem)
-    print("every-output parity", {"case": "moe_prefill", "dtype": str(dtype), "row_tiles": ntiles,
-                                  "outputs": int(yw.size), "rule_failures": int((~ok).sum()),
-                                  "max_ulp": round(rep["max_ulp"], 3), "oracle_s": round(t_orc, 2)}, flush=True)
-    assert ok.all(), rep
-    assert tolerance.in_outer_band(yw, S, A, wl.K, elem=elem).all()
+    # strict first (within one unit in the last place of the oracle's projection);
+    # band data (S, A) only for the rows holding outputs outside that
+    okp, repp = tolerance.check_proj(yw, y_ref, np.zeros(1), elem=elem)
+    rows = np.unique(np.nonzero(~okp)[0])
+    report = {"case": "moe_prefill", "dtype": str(dtype), "row_tiles": ntiles, "outputs": int(yw.size),
+              "proj_strict_over_1ulp": repp["n_fail"], "max_ulp": round(repp["max_ulp"], 3),
+              "rows_with_band_data": int(rows.size), "oracle_s": round(t_orc, 2)}
+    if rows.size:
+        S, A = orc.indexed_band(x[rows], w, idx.numpy()[rows], elem=elem)
+        ok, rep = tolerance.check_proj(yw[rows], y_ref[rows], A, elem=elem)
+        report["rule_failures"] = int((~ok).sum())
+        assert ok.all(), (report, rep)
+        assert tolerance.in_outer_band(yw[rows], S, A, wl.K, elem=elem).all(), report
+    print("every-output parity", report, flush=True)

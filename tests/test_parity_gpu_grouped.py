@@ -359,6 +359,35 @@ def test_indexed_absorbed_rows_bit_exact(orc, N, dtype):
     assert (s[~valid] == 0).all()
 
 
+def test_indexed_absorbed_rows_many_experts(orc):
+    """64 experts of 257 to 288 rows each at N = 4096: every expert's leftover rows
+    go into its one full tile (64 row tiles, 4 rounds of workgroups on 256 CUs,
+    instead of 128 tiles and 8 rounds), every tile holds between 257 and 288 rows,
+    and every output matches the oracle bit for bit on integer data."""
+    E, N, K = 64, 4096, 64
+    g = torch.Generator().manual_seed(64)
+    counts = torch.randint(257, 289, (E,), generator=g).tolist()
+    idx = torch.cat([torch.full((c,), e) for e, c in enumerate(counts)])
+    idx = idx[torch.randperm(idx.numel(), generator=g)].to(torch.int32)
+    M = idx.numel()
+    x, w = ints((M, K), 30, M + K, F16), ints((E, K, N), 30, E + N, F16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    absorb = (E * 16 + cus - 1) // cus < (2 * E * 16 + cus - 1) // cus
+    ws = torch.zeros(la.indexed_workspace_bytes(E, M), dtype=torch.uint8, device=DEV)
+    y = la.linear_f16_indexed(x.to(DEV), w.to(DEV), idx.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    table = ws.view(torch.int32).cpu().numpy()
+    ntiles = int(table[0])
+    assert ntiles == (E if absorb else 2 * E), ntiles
+    if absorb:
+        t0 = (WS_HEADER_WORDS + M + 3) & ~3
+        tiles = table[t0:t0 + 4 * ntiles].reshape(ntiles, 4)
+        assert sorted(tiles[:, 2].tolist()) == sorted(counts)
+    y_ref, _ = orc.indexed(x, w, idx.numpy(), elem=tolerance.F16)
+    ok = eq_words(words(y), y_ref, tolerance.F16)
+    assert ok.all(), (~ok).sum()
+
+
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 def test_indexed_reused_workspace(orc, dtype):
     """One caller-owned workspace through calls of different sizes and both row

@@ -405,14 +405,14 @@ indexed_routed(IndexedArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
 
     const int tiles_n = (a.N + BN - 1) / BN;
+    // the used (tile, column tile) pairs are the first workgroup ids; the rest
+    // exit.  Each XCD (ids are dealt round-robin over them) takes a contiguous
+    // run of the pairs, walked 4 row tiles at a time as in the dense kernel:
+    // the tiles running together on an XCD share x and panel reads in its L2.
+    const int ntiles = a.ws[0];
+    if ((int)blockIdx.x >= ntiles * tiles_n) return;  // an unused slot (uniform)
     int tv, tn;
-    // column tile fastest: the used slots come first and fill every XCD evenly
-    // (consecutive workgroup ids are dealt round-robin over the 8 XCDs), and the
-    // tiles of one expert that share a column panel share an XCD when tiles_n
-    // is a multiple of 8
-    tv = blockIdx.x / tiles_n;
-    tn = blockIdx.x - tv * tiles_n;
-    if (tv >= a.ws[0]) return;                        // an unused slot (uniform)
+    tile_coords(blockIdx.x, ntiles, tiles_n, a.xcd_shift, tv, tn);
     const int4 tile = ((const int4*)(a.ws + idx_ws_tiles(a.M)))[tv];
     const int32_t* list = a.ws + kIdxHeaderWords + tile.x;
     const int expert = tile.y, rows = tile.z;

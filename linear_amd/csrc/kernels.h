@@ -63,6 +63,7 @@ struct IndexedArgs {
     int vec_store;          // y takes 4-element vector stores
     int slots;              // routed path: row-tile slots in the grid (>= tiles used)
     int cus;                // compute units of the device (the routing pass's round size)
+    int xcd_shift;          // log2 of the device's XCD count (workgroup ids are dealt round-robin over them)
 };
 
 // Row-scan kernel (any layout): one workgroup per (expert, kIdxCols columns).

@@ -470,6 +470,7 @@ int32_t run_indexed(int elem, bool f32_out, const uint16_t* x, int64_t ldx, cons
     a.vec_store = ((uintptr_t)y % (f32_out ? 16 : 8) == 0) && (ldy % 4 == 0) ? 1 : 0;
     a.slots = 0;
     a.cus = di.cus;
+    a.xcd_shift = di.xcd_shift;
     const int mode = f32_out ? lin::kOutF32 : lin::kOutRound;
     hipError_t e;
     if (indexed_routed_ok(x, ldx, w, ldw, sw, E, M, N, K)) {

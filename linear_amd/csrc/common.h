@@ -62,17 +62,21 @@ enum : int { kF16 = 0, kBF16 = 1 };
 // epilogue program of a.epi.
 enum : int { kOutBias = 0, kOutRound = 1, kOutF32 = 2, kOutEpi = 3 };
 
-// Grouped contraction: workgroup z handles group z, the activation slice
-// x + z * gsx, the weight block of rows z * N .. z * N + N - 1, y + z * gsy and the
-// bias words z * N ...  (no-op for ungrouped launches, gridDim.z == 1).
+// Grouped contraction: group g is the activation slice x + g * gsx, the weight
+// block of rows g * N .. g * N + N - 1, y + g * gsy and the bias words g * N ..
 template <int MODE>
-__device__ inline void enter_group(LinearArgs& a) {
-    const int64_t g = blockIdx.z;
+__device__ inline void enter_group_at(LinearArgs& a, int64_t g) {
     if (g == 0) return;
     a.x += g * a.gsx;
     a.w += g * (int64_t)a.N * a.ldw;
     a.y = (void*)((char*)a.y + g * a.gsy * (MODE == kOutF32 ? 4 : 2));
     if (a.b) a.b += g * (int64_t)a.N;
+}
+
+// Workgroup z handles group z (no-op for ungrouped launches, gridDim.z == 1).
+template <int MODE>
+__device__ inline void enter_group(LinearArgs& a) {
+    enter_group_at<MODE>(a, blockIdx.z);
 }
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, no stride.

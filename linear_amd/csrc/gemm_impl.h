@@ -363,10 +363,28 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
 // i.e. row l / CPR, stored chunk l % CPR, so it fetches the logical chunk that the
 // swizzle puts there.  With BK = 64 every load instruction covers whole 128-byte
 // rows.
+// Tile (tm, tn) of this workgroup, with its group entered.  One group: the XCD
+// walk of tile_coords over blockIdx.x.  Several groups (grid z): the groups' row
+// tiles are stacked into one column of G x tiles_m row tiles and walked as one
+// grid in the order workgroups are dispatched (x fastest, then z), so the run of
+// tiles an XCD holds spans as few groups, and so as few panels, as it can.
+template <int MODE>
+__device__ inline void stream_tile(LinearArgs& a, int& tm, int& tn) {
+    if (gridDim.z == 1) {
+        tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
+        return;
+    }
+    const int tiles = a.tiles_m * a.tiles_n;
+    int row;
+    tile_coords(blockIdx.x + tiles * blockIdx.z, gridDim.z * a.tiles_m, a.tiles_n, a.xcd_shift, row, tn);
+    const int g = row / a.tiles_m;
+    tm = row - g * a.tiles_m;
+    enter_group_at<MODE>(a, g);
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_stream(LinearArgs a) {
-    enter_group<MODE>(a);
     constexpr int KS = BK / 16;                       // MFMA K steps per slice
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -392,7 +410,7 @@ gemm_stream(LinearArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDSB];
 
     int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
+    stream_tile<MODE>(a, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = a.K;
     const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n0, a.N, a.ldw, K);

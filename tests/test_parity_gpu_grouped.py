@@ -424,6 +424,21 @@ def test_indexed_empty_cases(orc):
     assert (words(y2) == words(torch.tensor([1.0], dtype=F16))[0]).all()
 
 
+@pytest.mark.parametrize("E,M,N,K", [(8, 4800, 4096, 4096), (16, 4096, 4096, 4096), (64, 8192, 2048, 2048)],
+                         ids=["8x4800", "16x4096", "64x8192"])
+def test_indexed_multi_round_sampled(orc, E, M, N, K):
+    """Routings that need more than one round of 256-row workgroups (24, about 24
+    and 64+ row tiles), walked per XCD: 48 rows (the first 8 and 40 at random)
+    against the oracle over every column, within the rule."""
+    x, w, idx = workloads.make_indexed_inputs(E, M, N, K, 1.0 / np.sqrt(K), seed=E + M, dtype=F16)
+    y = words(indexed(F16, x, w, idx))
+    rows = np.unique(np.concatenate([np.arange(8), np.random.default_rng(E).integers(0, M, 40)]))
+    y_ref, _ = orc.indexed(x[rows], w, idx.numpy()[rows], elem=tolerance.F16)
+    _, A = orc.indexed_band(x[rows], w, idx.numpy()[rows], elem=tolerance.F16)
+    ok, rep = tolerance.check_proj(y[rows], y_ref, A, elem=tolerance.F16)
+    assert ok.all(), rep
+
+
 @pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
 @pytest.mark.parametrize("name", ["moe_decode", "moe_prefill"])
 def test_indexed_workloads_sampled(orc, name, dtype):

@@ -672,6 +672,9 @@ def main():
     for kind in ("read", "empty", "mfma"):
         log("probe", kind)
         context["probe_" + kind] = bench_probe(kind, torch, workloads, stream)
+    # the decode launch's rate against a plain read of the same rotated weights on
+    # its grid, measured in this run: the part's practical ceiling for this call
+    context["decode_frac_of_probe_read"] = round(achieved / context["probe_read"]["gbs"], 4)
     log("context", json.dumps(context))
 
     prefill = {}

@@ -228,14 +228,25 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
     if (tid == 0) wsum[64] = wsum[65] = 0;
-    // idx is read 4 rows per thread at a time, the loads issued together
-    for (int m0 = 0; m0 < M; m0 += 4096) {
-        int e[4];
+    // idx is read 4 rows per thread at a time, the loads issued together; the
+    // first 4096 rows' values stay in registers for the row list below
+    auto load4 = [&](int m0, int (&e)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + 1024 * j + tid;
             const int v = idx[min(m, M - 1)];         // unconditional: the four loads go out together
             e[j] = m < M ? v : -1;
+        }
+    };
+    int e0[4];
+    load4(0, e0);
+    for (int m0 = 0; m0 < M; m0 += 4096) {
+        int e[4];
+        if (m0 == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = e0[j];
+        } else {
+            load4(m0, e);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -298,11 +309,11 @@ __global__ void __launch_bounds__(1024) indexed_route(const int32_t* __restrict_
     // row list: each row takes the next free slot of its expert
     for (int m0 = 0; m0 < M; m0 += 4096) {
         int e[4];
+        if (m0 == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + 1024 * j + tid;
-            const int v = idx[min(m, M - 1)];
-            e[j] = m < M ? v : -1;
+            for (int j = 0; j < 4; ++j) e[j] = e0[j];
+        } else {
+            load4(m0, e);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)

@@ -339,6 +339,25 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
     }
 }
 
+// Tile (tm, tn) of this workgroup, with its group entered.  One group: the XCD
+// walk of tile_coords over blockIdx.x.  Several groups (grid z): the groups' row
+// tiles are stacked into one column of G x tiles_m row tiles and walked as one
+// grid in the order workgroups are dispatched (x fastest, then z), so the run of
+// tiles an XCD holds spans as few groups, and so as few panels, as it can.
+template <int MODE>
+__device__ inline void stream_tile(LinearArgs& a, int& tm, int& tn) {
+    if (gridDim.z == 1) {
+        tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
+        return;
+    }
+    const int tiles = a.tiles_m * a.tiles_n;
+    int row;
+    tile_coords(blockIdx.x + tiles * blockIdx.z, gridDim.z * a.tiles_m, a.tiles_n, a.xcd_shift, row, tn);
+    const int g = row / a.tiles_m;
+    tm = row - g * a.tiles_m;
+    enter_group_at<MODE>(a, g);
+}
+
 // ---------------------------------------------------------------------------
 // Streaming variant for 16-byte aligned layouts (x, weight 16-byte aligned, ldx,
 // ldw and K multiples of 8).
@@ -363,26 +382,13 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
 // i.e. row l / CPR, stored chunk l % CPR, so it fetches the logical chunk that the
 // swizzle puts there.  With BK = 64 every load instruction covers whole 128-byte
 // rows.
-// Tile (tm, tn) of this workgroup, with its group entered.  One group: the XCD
-// walk of tile_coords over blockIdx.x.  Several groups (grid z): the groups' row
-// tiles are stacked into one column of G x tiles_m row tiles and walked as one
-// grid in the order workgroups are dispatched (x fastest, then z), so the run of
-// tiles an XCD holds spans as few groups, and so as few panels, as it can.
-template <int MODE>
-__device__ inline void stream_tile(LinearArgs& a, int& tm, int& tn) {
-    if (gridDim.z == 1) {
-        tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.xcd_shift, tm, tn);
-        return;
-    }
-    const int tiles = a.tiles_m * a.tiles_n;
-    int row;
-    tile_coords(blockIdx.x + tiles * blockIdx.z, gridDim.z * a.tiles_m, a.tiles_n, a.xcd_shift, row, tn);
-    const int g = row / a.tiles_m;
-    tm = row - g * a.tiles_m;
-    enter_group_at<MODE>(a, g);
-}
-
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1>
+//
+// WHOLE (tiles with one MFMA per wave and K step): a K step's fragment reads
+// would have a single MFMA to hide behind, so each slice's fragments are read at
+// once and its MFMAs run as they land; and only slices that exist are requested,
+// the wait for slice t choosing at run time how many later slices may still be
+// in flight (no zero-fill requests past K).
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1, bool WHOLE = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_stream(LinearArgs a) {
     constexpr int KS = BK / 16;                       // MFMA K steps per slice
@@ -493,7 +499,45 @@ gemm_stream(LinearArgs a) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
 
-    if (nk > 0) {
+    if constexpr (WHOLE) {
+        // at most c (< STAGES, uniform) slices' requests left in flight
+        auto wait_behind = [&](int c) {
+            static_for<0, STAGES>([&]<int k>() {
+                if (c == k) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(k * GPW) : "memory");
+            });
+        };
+        if (nk > 0) {
+            const int pro = nk < STAGES ? nk : STAGES;
+            for (int t = 0; t < pro; ++t) static_for<0, GPW>([&]<int j>() { LIN_ISSUE_ONE(t, j); });
+            wait_behind(pro - 1);
+            lds_barrier();
+        }
+        for (int t = 0; t < nk; ++t) {
+            // slot t - 1 is refilled once the barrier shows that slice t has
+            // landed and that every wave has read slice t - 1
+            if (t > 0) {
+                wait_behind(min(STAGES - 2, nk - 1 - t));
+                lds_barrier();
+            }
+            const unsigned char* slot = smem + (t % STAGES) * SLICE;
+            u32x4 fa[KS][FN], fb[KS][FM];
+            static_for<0, KS>([&]<int ks>() {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) fa[ks][i] = *(const u32x4*)(slot + aoff[ks][i]);
+#pragma unroll
+                for (int j = 0; j < FM; ++j) fb[ks][j] = *(const u32x4*)(slot + boff[ks][j]);
+            });
+            __builtin_amdgcn_sched_barrier(0);   // every read issued before the refill and the MFMAs
+            if (t > 0 && t - 1 + STAGES < nk) static_for<0, GPW>([&]<int j>() { LIN_ISSUE_ONE(t - 1 + STAGES, j); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, KS>([&]<int ks>() {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16<E>(fa[ks][i], fb[ks][j], acc[i][j]);
+            });
+        }
+    } else if (nk > 0) {
         // Requests past the last slice carry out-of-range offsets (zero fill, no
         // memory traffic), so the number of requests behind any slice is fixed and
         // every wait below is static.  The prologue issues slices 0 .. STAGES-2 and
@@ -574,12 +618,12 @@ static const void* regstaged_fn(int mode) {
     return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutF32>;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD, bool WHOLE = false>
 static const void* stream_fn(int mode) {
-    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD>;
-    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD>;
-    if (mode == kOutEpi) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutEpi, SPREAD>;
-    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD>;
+    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD, WHOLE>;
+    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD, WHOLE>;
+    if (mode == kOutEpi) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutEpi, SPREAD, WHOLE>;
+    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD, WHOLE>;
 }
 
 static hipError_t launch(const void* fn, const LinearArgs& a, int threads, hipStream_t stream) {
@@ -603,13 +647,14 @@ hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStrea
     switch (cfg) {
         // load spread (K steps a slice's refill is spread over), measured per tile
         // with the ring's own barriers: 256 x 256 best at 1, 256 x 128 and 128 x 128
-        // at 2 (down 241 -> 222 us), 64 x 64 at 1; 128 x 256 (32-wide slices)
-        // has no step to spare
+        // at 2 (down 241 -> 222 us); 128 x 256 (32-wide slices) has no step to
+        // spare.  64 x 64 reads whole slices (toy layer: 6.94 us per call against
+        // 7.17 pipelined; rings of 3, 5 or 6 slots 7.6-8.1)
         case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E, 1>(mode), a, 512, stream);
         case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E, 2>(mode), a, 512, stream);
         case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E, 0>(mode), a, 512, stream);
         case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E, 2>(mode), a, 256, stream);
-        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E, 1>(mode), a, 256, stream);
+        case 4: return launch(stream_fn<64, 64, 2, 2, 4, 64, E, 0, true>(mode), a, 256, stream);
         default: return hipErrorInvalidValue;
     }
 }

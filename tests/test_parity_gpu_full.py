@@ -102,6 +102,8 @@ TILE_SHAPES = [
     (3990, 1910, 40, (128, 256), False),
     (2000, 2000, 200, (128, 128), False),
     (1000, 1000, 104, (64, 64), False),
+    (333, 900, 136, (64, 64), False),         # three slices, fewer than the ring's four slots
+    (600, 520, 192, (64, 64), False),
     (1000, 1000, 1032, (64, 64), False),
     (77, 1100, 8, (64, 64), False),           # one K slice, most of it past K
     (8192, 4096, 24, (256, 256), False),      # attn's tile at a short K

@@ -471,7 +471,8 @@ def _probe_lib():
     lib.probe_read.argtypes = [vp, i64, i32, vp, vp]
     lib.probe_empty.argtypes = [i32, vp]
     lib.probe_mfma.argtypes = [vp, i32, i32, vp, vp]
-    for f in (lib.probe_read, lib.probe_empty, lib.probe_mfma):
+    lib.probe_loads.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    for f in (lib.probe_read, lib.probe_empty, lib.probe_mfma, lib.probe_loads):
         f.restype = i32
     return lib
 
@@ -484,7 +485,11 @@ def bench_probe(kind, torch, workloads, stream):
              decode kernel's grid (256 workgroups of 512 threads);
       empty: an empty kernel on that grid (the per-launch floor);
       mfma:  register-only v_mfma_f32_32x32x16_f16 on random binary16 operands
-             (1024 workgroups of 4 waves, 2000 rounds of 8 MFMAs per wave)."""
+             (1024 workgroups of 4 waves, 2000 rounds of 8 MFMAs per wave);
+      loads_attn, loads_toy: the streaming GEMM's operand loads alone for the
+             attention projection (256 x 256 tiles, 2 slots) and the toy layer
+             (64 x 64 tiles, 4 slots), no fragment reads and no MFMAs, with the
+             inputs rotating as in those shapes' own benchmarks."""
     lib = _probe_lib()
     sp = ctypes_stream(stream)
     if kind == "read":
@@ -511,11 +516,26 @@ def bench_probe(kind, torch, workloads, stream):
         def call(i):
             assert lib.probe_mfma(ops.data_ptr(), grid, iters, out.data_ptr(), sp) == 0
         calls, per = 8, 0
+    elif kind in ("loads_attn", "loads_toy"):
+        name, tile, bm = ("attn", 0, 256) if kind == "loads_attn" else ("toy", 1, 64)
+        wl = workloads.WORKLOADS[name]
+        x, w, _ = workloads.workload_inputs(name, seed=0, device="cuda")
+        sets = rotation_sets(wl.bytes)          # the same rotation as the layer's own benchmark
+        xs = [x] + [x.clone() for _ in range(sets - 1)]
+        ws = [w] + [w.clone() for _ in range(sets - 1)]
+        tiles = (wl.M // bm) * (wl.N // bm)
+        sink = torch.zeros(tiles, dtype=torch.int32, device="cuda")
+
+        def call(i):
+            rc = lib.probe_loads(xs[i % sets].data_ptr(), ws[i % sets].data_ptr(), wl.M, wl.N, wl.K, tile,
+                                 sink.data_ptr(), sp)
+            assert rc == 0, rc
+        calls, per = graph_calls(sets), tiles * 2 * bm * wl.K * 2
     else:
         raise SystemExit("unknown probe %s" % kind)
     graph = capture(call, calls, stream, torch)
     graph.replay()
-    replays = max(1, 640 // calls) if kind != "mfma" else 4
+    replays = 4 if kind in ("mfma", "loads_attn") else max(1, 640 // calls)
     times = [time_region(graph, replays, stream, torch) for _ in range(5)]
     us = sorted(times)[2] / (replays * calls) * 1e3
     del graph
@@ -524,6 +544,10 @@ def bench_probe(kind, torch, workloads, stream):
     if kind == "read":
         r.update({"bytes_per_launch": per, "gbs": round(per / (us * 1e-6) / 1e9, 1),
                   "frac_hbm_peak": round(per / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": copies})
+    if kind.startswith("loads_"):
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        r.update({"name": name, "tile": [bm, bm], "input_sets": sets, "bytes_into_cus_per_launch": per,
+                  "gbs_per_cu": round(per / cus / (us * 1e-6) / 1e9, 1)})
     if kind == "mfma":
         flops = grid * 4 * iters * 8 * 32768.0
         r.update({"flops_per_launch": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
@@ -683,6 +707,14 @@ def main():
             log("prefill", name)
             prefill[name] = bench_gemm(name, torch, la, workloads, stream, calls)
             log(json.dumps(prefill[name]))
+        # the same calls' operand loads alone (probe kernels, same tiles, ring and
+        # input rotation, no MFMAs): what share of each call the loads account for
+        for kind, name in (("loads_toy", "toy"), ("loads_attn", "attn")):
+            log("probe", kind)
+            r = bench_probe(kind, torch, workloads, stream)
+            r["frac_of_call"] = round(r["us_per_launch"] / prefill[name]["us_per_call"], 4)
+            prefill[name]["operand_loads_alone"] = r
+            log(json.dumps(r))
     variants = {}
     if not args.no_variants:
         dargs = argparse.Namespace(steps=args.steps, warmup=args.warmup, repeats=args.repeats)

@@ -9,6 +9,9 @@
 //  - probe_mfma: v_mfma_f32_32x32x16_f16 on register operands only (no memory
 //    traffic inside the loop), the matrix-core rate this part sustains on real
 //    data at its power-limited clock.
+//  - probe_loads: the streaming GEMM's operand loads alone (its tile, its ring of
+//    64-wide K slices, its direct-to-LDS loads, waits, barriers and XCD tile walk,
+//    no fragment reads and no MFMAs): how fast the operands of a tile reach a CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,6 +52,77 @@ __global__ void __launch_bounds__(kThreads) probe_read_kernel(const u32x4* src, 
 }
 
 __global__ void __launch_bounds__(kThreads) probe_empty_kernel() {}
+
+// Tile t of a tiles_m x tiles_n grid for workgroup bid: workgroups are dealt
+// round-robin over 2^xcd_shift XCDs, each XCD takes a contiguous run of tiles,
+// walked 4 tile-rows at a time (the streaming GEMM's order).
+__device__ inline void probe_tile(int bid, int tiles_m, int tiles_n, int xcd_shift, int& tm, int& tn) {
+    const int G = tiles_m * tiles_n, xmask = (1 << xcd_shift) - 1;
+    const int xcd = bid & xmask, idx = bid >> xcd_shift;
+    const int q = G >> xcd_shift, r = G & xmask;
+    const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    const int per_group = 4 * tiles_n, g = t / per_group, first_m = g * 4;
+    const int gm = min(tiles_m - first_m, 4), rem = t - g * per_group;
+    tm = first_m + rem % gm;
+    tn = rem / gm;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The operand loads of a BM x BN tile over all of K (a multiple of 64): slice s
+// (64 K values, 128 bytes of each of the tile's BN weight rows and BM x rows) goes
+// into LDS slot s % STAGES as (BM + BN) / 8 direct loads of 8 rows x 128 bytes.
+// Slices 0 .. STAGES-1 are requested at once; slot s - 1 is refilled with slice
+// s - 1 + STAGES once slice s has landed in every wave (wait, then barrier), as
+// the GEMM refills a slot after the barrier that follows its last reads.  Only
+// slices that exist are requested.  One LDS word per workgroup goes to sink.
+template <int BM, int BN, int NW, int STAGES>
+__global__ void __launch_bounds__(NW * 64) probe_loads_kernel(const uint16_t* x, const uint16_t* w, int M, int N,
+                                                              int K, int xcd_shift, uint32_t* sink) {
+    constexpr int SLICE = (BM + BN) * 128, GPW = (BM + BN) / 8 / NW;
+    static_assert((BM + BN) / 8 % NW == 0 && STAGES * SLICE <= 160 * 1024, "probe tile");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * SLICE];
+    int tm, tn;
+    probe_tile(blockIdx.x, M / BM, N / BN, xcd_shift, tm, tn);
+    const int64_t bytes_w = (int64_t)BN * K * 2, bytes_x = (int64_t)BM * K * 2;
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(w + (int64_t)tn * BN * K), (short)0, (int)bytes_w, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)tm * BM * K), (short)0, (int)bytes_x, 0x00020000);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nk = K / 64;
+    auto issue = [&](int s) {
+        unsigned char* slot = smem + (s % STAGES) * SLICE;
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            const int g = wave * GPW + j;
+            const bool isw = g < BN / 8;
+            const int r = (isw ? g : g - BN / 8) * 8 + lane / 8;
+            const uint32_t off = (uint32_t)(((int64_t)r * K + s * 64 + (lane % 8) * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isw ? rw : rx, (lds_void*)(slot + g * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    // at most c (< STAGES) slices' loads left in flight
+    auto wait_behind = [&](int c) {
+        if (c <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (c == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GPW) : "memory");
+        else if (c == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * GPW) : "memory");
+    };
+    static_assert(STAGES <= 4 && 3 * GPW < 64, "waits cover rings of up to 4 slots");
+    const int pro = nk < STAGES ? nk : STAGES;
+    for (int s = 0; s < pro; ++s) issue(s);
+    wait_behind(pro - 1);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int t = 1; t < nk; ++t) {
+        wait_behind(min(STAGES - 2, nk - 1 - t));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (t - 1 + STAGES < nk) issue(t - 1 + STAGES);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = *(const uint32_t*)(smem + ((nk - 1) % STAGES) * SLICE);
+}
 
 // Each wave keeps 4 independent accumulators and runs `iters` rounds of 8 MFMAs
 // on operands loaded once from `ops` (random binary16 data: the matrix unit's
@@ -101,6 +175,35 @@ int32_t probe_read(const void* src, int64_t bytes, int32_t grid, uint32_t* sink,
 int32_t probe_empty(int32_t grid, void* stream) {
     if (grid <= 0) return -1;
     hipLaunchKernelGGL(probe_empty_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream);
+    return (int32_t)hipGetLastError();
+}
+
+// The operand loads of the streaming GEMM's tile over x [M, K] and weight [N, K]
+// (both row-major, 16-byte aligned, row stride K): tile 0 is 256 x 256 (8 waves,
+// 2 slots), tile 1 is 64 x 64 (4 waves, 4 slots).  M and N must be multiples of
+// the tile, K a positive multiple of 64 with 256 K * 2 bytes below 2 GiB; sink
+// holds one word per tile.  The tile walk takes the current device's XCD count,
+// as the library does.  Returns 0, -1 for a shape it does not take, or the HIP
+// error.
+int32_t probe_loads(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t tile, uint32_t* sink,
+                    void* stream) {
+    if (!x || !w || !sink || K <= 0 || K % 64 != 0 || (int64_t)256 * K * 2 >= ((int64_t)1 << 31)) return -1;
+    int dev = 0, xcds = 1, xcd_shift = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) xcds = 1;
+    while ((2 << xcd_shift) <= xcds) ++xcd_shift;
+    if ((1 << xcd_shift) != xcds) xcd_shift = 0;
+    if (tile == 0) {
+        if (M <= 0 || N <= 0 || M % 256 != 0 || N % 256 != 0) return -1;
+        hipLaunchKernelGGL((probe_loads_kernel<256, 256, 8, 2>), dim3((M / 256) * (N / 256)), dim3(512), 0,
+                           (hipStream_t)stream, (const uint16_t*)x, (const uint16_t*)w, M, N, K, xcd_shift, sink);
+    } else if (tile == 1) {
+        if (M <= 0 || N <= 0 || M % 64 != 0 || N % 64 != 0) return -1;
+        hipLaunchKernelGGL((probe_loads_kernel<64, 64, 4, 4>), dim3((M / 64) * (N / 64)), dim3(256), 0,
+                           (hipStream_t)stream, (const uint16_t*)x, (const uint16_t*)w, M, N, K, xcd_shift, sink);
+    } else {
+        return -1;
+    }
     return (int32_t)hipGetLastError();
 }
 

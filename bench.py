@@ -39,14 +39,17 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPYCAL_BYTES = (64 << 20) * 4   # one copy in --only copycal: 64 Mi float32 read and written
 # sources whose change invalidates recorded counter readings, per kernel
 KERNEL_SOURCES = {
-    "skinny_f16_stream": ["linear_amd/csrc/skinny.hip", "linear_amd/csrc/common.h"],
+    "decode_f16_step": ["linear_amd/csrc/skinny.hip", "linear_amd/csrc/common.h"],
     "gemm_f16_stream": ["linear_amd/csrc/gemm_impl.h", "linear_amd/csrc/gemm_f16.hip",
                         "linear_amd/csrc/common.h"],
 }
-# substring of the demangled kernel name that each recorded kernel's counter rows carry
+# substrings of the demangled kernel names whose counter rows a record averages
+# over (per dispatch)
 KERNEL_PATTERNS = {
-    "skinny_f16_stream": "skinny_stream<8, 0, 0>",   # 8 waves, binary16, bias epilogue
-    "gemm_f16_stream": "gemm_stream<",
+    # the decode step's two launches, binary16 with the bias step: M = 1 on the
+    # one-row kernel, M = 16 on the 16-row kernel (8 waves)
+    "decode_f16_step": ("gemv_stream<0, 0>", "skinny_stream<8, 0, 0>"),
+    "gemm_f16_stream": ("gemm_stream<",),
 }
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense FP16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 ROTATE_BYTES = 512 * 1024 * 1024
@@ -100,13 +103,20 @@ def record_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: 
                    commands: list[str]):
     """Turn FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of `kernel` and of the plain
     copy calibration into bytes per launch, and store them with a hash of the kernel
-    sources so that a later change of the kernel invalidates them."""
-    def pick(d, counter, name):
+    sources so that a later change of the kernel invalidates them.  A record over
+    several kernels (KERNEL_PATTERNS) averages their per-dispatch means."""
+    def pick(d, counter, names):
+        if isinstance(names, str):
+            names = (names,)
         m = _counter_means(d, counter)
-        hits = [(k, v) for k, v in m.items() if name in k]
+        hits = [(k, v) for k, v in m.items() if any(n in k for n in names)]
         if not hits:
-            raise SystemExit("no %s dispatches of %s under %s" % (counter, name, d))
-        return hits[0]
+            raise SystemExit("no %s dispatches of %s under %s" % (counter, " or ".join(names), d))
+        # each matching kernel counts once (one launch each per unit of work, e.g.
+        # the decode step's M = 1 and M = 16 calls), whatever its dispatch count
+        n = sum(c for _, (_, c) in hits)
+        mean = sum(v for _, (v, _) in hits) / len(hits)
+        return " + ".join(sorted(k for k, _ in hits)), (mean, n)
     kname, (fetch_kib, nf) = pick(fetch_dir, "FETCH_SIZE", KERNEL_PATTERNS[kernel])
     _, (write_kib, nw) = pick(write_dir, "WRITE_SIZE", KERNEL_PATTERNS[kernel])
     _, (cf_kib, _) = pick(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
@@ -772,8 +782,9 @@ def main():
                                                                detail["graph_replays"]["remainder_steps"]),
             "warmup_as": "%d steps replayed through the same graphs (plus %d steps run eagerly while "
                          "capturing them)" % (args.warmup, detail["eager_steps_at_capture"]),
-            "kernel": "skinny_stream<8, f16, bias> (16 output columns x 16 rows per workgroup, 8 waves, "
-                      "v_mfma_f32_16x16x32_f16)",
+            "kernel": "M = 1: gemv_stream<f16, bias> (one wave per weight row, 4 rows per workgroup, FP32 "
+                      "FMAs); M = 16: skinny_stream<8, f16, bias> (16 output columns x 16 rows per workgroup, "
+                      "8 waves, v_mfma_f32_16x16x32_f16)",
         },
         "roofline": {
             "bound": "hbm",
@@ -781,8 +792,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("skinny_f16_stream"),
-            "kernel": "skinny_f16_stream",
+            "traffic": recorded_traffic("decode_f16_step"),
+            "kernel": "decode_f16_step: gemv_stream (M = 1) and skinny_stream (M = 16), one launch each",
             "bytes_per_launch": per_launch_bytes,
             "us_per_launch": round(per_launch_s * 1e6, 3),
         },

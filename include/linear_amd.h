@@ -82,7 +82,9 @@ extern "C" {
  */
 #define LINEAR_PATH_AUTO   0  /* M <= 16: skinny path; otherwise the MFMA tiled GEMM */
 #define LINEAR_PATH_GEMM   1  /* force the MFMA tiled GEMM (any M) */
-#define LINEAR_PATH_SKINNY 2  /* force the weight-streaming skinny path (any M, 16 rows per block) */
+#define LINEAR_PATH_SKINNY 2  /* force the weight-streaming skinny path (any M, 16 rows per block;
+                                 at M == 1 with the fast-path layout, no epilogue program, one group
+                                 and K <= 32768: one wave per weight row, 4 rows per block) */
 
 /*
  * y = FP16(FP16(x . weight^T) + b).  See the conventions above.
@@ -366,7 +368,8 @@ typedef struct linear_plan {
     int32_t path;       /* LINEAR_PATH_GEMM or LINEAR_PATH_SKINNY */
     int32_t tile_m;     /* output rows (m) per workgroup */
     int32_t tile_n;     /* output columns (n) per workgroup */
-    int32_t tile_k;     /* K elements per main-loop stage (GEMM) or per wave step (skinny) */
+    int32_t tile_k;     /* K elements per main-loop stage (GEMM), per wave step (skinny) or per wave
+                           load (skinny at M == 1: tile_m 1, tile_n 4) */
     int32_t threads;    /* threads per workgroup */
     int32_t vector_io;  /* 1: 16-byte loads; 0: element-wise loader */
     int64_t grid;       /* workgroups launched (the first launch when split) */

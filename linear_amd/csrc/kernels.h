@@ -49,6 +49,14 @@ constexpr int kSkinnyTile = 16;
 constexpr int kSkinnyKStep = 32;
 hipError_t launch_skinny(int elem, const LinearArgs& a, bool vec, int mode, hipStream_t stream);
 
+// One-row kernel of the skinny path (M = 1, 16-byte aligned layouts, ungrouped,
+// no epilogue program, K <= kGemvMaxK): one wave per weight row, kGemvRows rows
+// per workgroup, x staged in LDS (K * 2 bytes of dynamic shared memory).
+constexpr int kGemvRows = 4;
+constexpr int kGemvSeg = 512;      // K values per 1 KB wave load (64 lanes x 8)
+constexpr int kGemvMaxK = 32768;   // 64 KB of x in LDS
+hipError_t launch_gemv(int elem, const LinearArgs& a, int mode, hipStream_t stream);
+
 // Indexed contraction (x [M, K] against expert tables W [E, K, N], row m against
 // expert idx[m]).
 struct IndexedArgs {

@@ -144,6 +144,12 @@ bool vector_loads_ok(const Request& r) {
            (r.ldw % 8 == 0) && (r.K % 8 == 0) && (r.G <= 1 || r.sx % 8 == 0);
 }
 
+// The skinny path's one-row kernel: a single x row, 16-byte loads, one group,
+// no epilogue program, x small enough to stage in LDS.
+bool one_row_kernel(const Request& r) {
+    return r.M == 1 && r.G <= 1 && !r.epi && r.K <= lin::kGemvMaxK && vector_loads_ok(r);
+}
+
 bool vector_store_ok(const Request& r) {
     return ((uintptr_t)r.y % (r.f32_out ? 16 : 8) == 0) && (r.ldy % 4 == 0) && (r.G <= 1 || r.sy % 4 == 0);
 }
@@ -223,7 +229,14 @@ int32_t plan(const Request& r, linear_plan* p, int cus) {
     if (path == LINEAR_PATH_AUTO) path = (r.M <= kSkinnyMaxM) ? LINEAR_PATH_SKINNY : LINEAR_PATH_GEMM;
     p->path = path;
     p->vector_io = vector_loads_ok(r) ? 1 : 0;
-    if (path == LINEAR_PATH_SKINNY) {
+    if (path == LINEAR_PATH_SKINNY && one_row_kernel(r)) {
+        p->tile_m = 1;
+        p->tile_n = lin::kGemvRows;
+        p->tile_k = lin::kGemvSeg;
+        p->threads = lin::kGemvRows * 64;
+        p->grid = (r.N + lin::kGemvRows - 1) / lin::kGemvRows;
+        if (p->grid > kMaxGridX) return LINEAR_E_SHAPE;
+    } else if (path == LINEAR_PATH_SKINNY) {
         p->tile_m = lin::kSkinnyTile;
         p->tile_n = lin::kSkinnyTile;
         p->tile_k = lin::kSkinnyKStep;
@@ -371,7 +384,8 @@ int32_t run(const Request& r, void* stream) {
     if (p.path == LINEAR_PATH_SKINNY) {
         a.tiles_m = (int)((r.M + 15) / 16);
         a.tiles_n = (int)((r.N + 15) / 16);
-        e = lin::launch_skinny(r.elem, a, vec, mode, (hipStream_t)stream);
+        e = one_row_kernel(r) ? lin::launch_gemv(r.elem, a, mode, (hipStream_t)stream)
+                              : lin::launch_skinny(r.elem, a, vec, mode, (hipStream_t)stream);
     } else if (vec) {
         const int c = choose_stream_config(r.M, r.N, r.G, di.cus);
         const lin::GemmConfig& g = lin::kStreamConfigs[c];

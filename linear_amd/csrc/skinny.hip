@@ -27,6 +27,20 @@
 //    fragment as it arrives.
 //  - skinny_kernel (any layout): element-wise masked loads of both operands.
 // Both request the bias words of the finishing wave before the main loop.
+//
+// A third kernel, gemv_stream, takes M = 1 (16-byte aligned, ungrouped, no
+// epilogue program, K up to kGemvMaxK).  There x is a single row, so nothing is
+// gained by sharing it between weight rows through an MFMA, and the weight can be
+// streamed the way a plain read streams a buffer fastest on this part: many
+// small workgroups, each wave one weight row with all of its loads in flight.
+// Wave w of workgroup g owns row n = kGemvRows g + w; segment s of the row (K
+// values [512 s, 512 s + 512), 16 bytes per lane) is one 1 KB load.  The
+// workgroup first copies x into LDS; each lane multiplies its 8 weight values of
+// a segment by the matching x values in FP32 (exact products: 11-bit or 8-bit
+// significands) and adds them in K order into one of 8 sums (segment s into sum
+// s mod 8, which keeps the dependent FMA chains short); the 8 sums are added in
+// order, then the 64 lanes' by a fixed butterfly, and lane 0 rounds the full-K
+// sum and runs the bias step.  A fixed order throughout: deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -172,6 +186,90 @@ skinny_kernel(LinearArgs a) {
     } else {
         if (m < a.M) store4<E, MODE>(a, m, nb, s[0], s[1], s[2], s[3], bias);
     }
+}
+
+template <int E, int MODE>
+__global__ void __launch_bounds__(kGemvRows * 64)
+gemv_stream(LinearArgs a) {
+    constexpr int U = 8;                      // segments (1 KB loads per wave) in flight per pass
+    extern __shared__ __attribute__((aligned(16))) unsigned char xs_row[];   // x: K * 2 bytes
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);        // uniform
+    const int n = blockIdx.x * kGemvRows + wave;
+    const int K = a.K;
+    const int S = (K + kGemvSeg - 1) / kGemvSeg;
+    const __amdgpu_buffer_rsrc_t rx = matrix_rsrc(a.x, 0, 1, a.ldx, K);
+    const __amdgpu_buffer_rsrc_t rw = matrix_rsrc(a.w, n < a.N ? n : a.N, a.N, a.ldw, K);   // empty past N
+    // the bias word, requested first and widened only at the end (zero past N)
+    uint32_t bword = 0;
+    if constexpr (MODE == kOutBias) {
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)a.b, (short)0, a.N * 2, kRsrcWord3);
+        bword = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)n * 2u, 0, 0);
+    }
+    // x into LDS, segment s by wave s % kGemvRows
+    for (int s = wave; s < S; s += kGemvRows) {
+        const int k = s * kGemvSeg + lane * 8;
+        lds_dma16(rx, xs_row + s * 1024, k < K ? (uint32_t)k * 2u : kOOB);
+    }
+    float sums[U] = {};
+    for (int p = 0; p < S; p += U) {
+        u32x4 wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (p + u) * kGemvSeg + lane * 8;
+            wv[u] = load16(rw, (p + u < S && k < K) ? (uint32_t)k * 2u : kOOB);
+        }
+        __builtin_amdgcn_sched_barrier(0);    // every load of the pass in flight before any use
+        if (p == 0) {
+            // this wave's x copies were issued before the weight loads: wait for
+            // them alone, then for every wave's
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(U) : "memory");
+            lds_barrier();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = p + u;
+            // a segment past K has zero weights (out-of-range loads): any x will do
+            const u32x4 xv = *(const u32x4*)(xs_row + (s < S ? s : S - 1) * 1024 + lane * 16);
+            float acc = sums[u];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = __builtin_fmaf(widen<E>((uint16_t)wv[u][q]), widen<E>((uint16_t)xv[q]), acc);
+                acc = __builtin_fmaf(widen<E>((uint16_t)(wv[u][q] >> 16)), widen<E>((uint16_t)(xv[q] >> 16)), acc);
+            }
+            sums[u] = acc;
+        }
+    }
+    float acc = sums[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) acc += sums[u];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane != 0 || n >= a.N) return;
+    if constexpr (MODE == kOutF32) {
+        ((float*)a.y)[n] = acc;
+    } else {
+        uint16_t t = narrow<E>(acc);
+        if constexpr (MODE == kOutBias) t = narrow<E>(widen<E>(t) + widen<E>((uint16_t)bword));
+        ((uint16_t*)a.y)[n] = t;
+    }
+}
+
+template <int E>
+static const void* gemv_fn(int mode) {
+    if (mode == kOutBias) return (const void*)gemv_stream<E, kOutBias>;
+    if (mode == kOutRound) return (const void*)gemv_stream<E, kOutRound>;
+    return (const void*)gemv_stream<E, kOutF32>;
+}
+
+hipError_t launch_gemv(int elem, const LinearArgs& a, int mode, hipStream_t stream) {
+    if (a.M != 1 || a.groups > 1 || mode == kOutEpi || a.K > kGemvMaxK) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.N + kGemvRows - 1) / kGemvRows)), block(kGemvRows * 64);
+    LinearArgs args = a;
+    void* params[] = {&args};
+    const void* fn = elem == kBF16 ? gemv_fn<kBF16>(mode) : gemv_fn<kF16>(mode);
+    const size_t lds = (size_t)((a.K + kGemvSeg - 1) / kGemvSeg) * 1024;
+    return hipLaunchKernel(fn, grid, block, params, lds, stream);
 }
 
 template <int E>

@@ -299,6 +299,15 @@ def test_plans_for_the_workloads():
     assert (p["tile_m"], p["tile_n"], p["threads"], p["stages"], p["tile_k"], p["grid"]) == (64, 64, 256, 4, 64, 256)
     assert plan(8192, 4096, 4096)["stages"] == 2 and plan(2000, 4000, 14336)["stages"] == 3
     assert plan(16, 4096, 4096)["stages"] == 0                # the skinny path has no ring
+    # a single x row: one wave per weight row, 4 rows per workgroup, 512 K per wave load
+    p = plan(1, 4096, 4096)
+    assert (p["path"], p["tile_m"], p["tile_n"], p["tile_k"], p["threads"], p["grid"]) == (la.PATH_SKINNY, 1, 4, 512,
+                                                                                          256, 1024)
+    assert plan(1, 4097, 32768)["grid"] == 1025
+    assert plan(1, 64, 32776)["tile_m"] == 16                  # x too long to stage: the 16-row kernel
+    assert plan(1, 64, 63)["tile_m"] == 16                     # no 16-byte loads
+    assert plan(2, 4096, 4096)["tile_m"] == 16
+    assert plan(1, 64, 64, path=la.PATH_SKINNY)["tile_m"] == 1
 
 
 @needs_lib

@@ -33,7 +33,7 @@ def sandbox(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "traffic.json"))
     monkeypatch.setattr(bench, "KERNEL_SOURCES", {"k": ["k.hip"]})
-    monkeypatch.setattr(bench, "KERNEL_PATTERNS", {"k": "my_kernel<8>"})
+    monkeypatch.setattr(bench, "KERNEL_PATTERNS", {"k": ("my_kernel<8>",), "k2": ("my_kernel<8>", "their_kernel<1>")})
     return tmp_path
 
 
@@ -58,6 +58,25 @@ def test_traffic_record_scales_by_the_copy_calibration(sandbox, capsys):
     assert bench.recorded_traffic("k") == rec["bytes_per_launch"]
 
 
+def test_traffic_record_averages_over_its_kernels(sandbox, monkeypatch, capsys):
+    t = sandbox
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", {"k2": ["k.hip"]})
+    # one kernel twice at 1000 KiB, the other once at 400 KiB: each kernel counts once, 700 KiB
+    write_counters(t / "f", "FETCH_SIZE", [("void my_kernel<8>(Args)", 1000.0), ("void my_kernel<8>(Args)", 1000.0),
+                                          ("void their_kernel<1>(Args)", 400.0), ("void other(Args)", 5.0)])
+    write_counters(t / "w", "WRITE_SIZE", [("void my_kernel<8>(Args)", 10.0), ("void their_kernel<1>(Args)", 10.0)])
+    copy = bench.COPYCAL_BYTES / 1024.0
+    write_counters(t / "cf", "FETCH_SIZE", [("copyBuffer", copy)])
+    write_counters(t / "cw", "WRITE_SIZE", [("copyBuffer", copy)])
+    bench.record_traffic("k2", str(t / "f"), str(t / "w"), str(t / "cf"), str(t / "cw"), ["cmd"])
+    capsys.readouterr()
+    rec = json.load(open(bench.TRAFFIC_JSON))["k2"]
+    assert rec["dispatches"] == [3, 2]
+    assert rec["fetch_kib_per_dispatch"] == pytest.approx(700.0)
+    assert "my_kernel<8>" in rec["kernel_name"] and "their_kernel<1>" in rec["kernel_name"]
+    assert "other" not in rec["kernel_name"]
+
+
 def test_traffic_record_is_void_once_the_kernel_changes(sandbox, capsys):
     t = sandbox
     for d, c in (("f", "FETCH_SIZE"), ("w", "WRITE_SIZE")):
@@ -75,8 +94,8 @@ def test_traffic_record_is_void_once_the_kernel_changes(sandbox, capsys):
 def test_committed_traffic_record_names_its_kernel():
     """The committed record covers the decode kernel, with the commands that made it."""
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
-    r = rec["skinny_f16_stream"]
-    assert bench.KERNEL_PATTERNS["skinny_f16_stream"] in r["kernel_name"]
+    r = rec["decode_f16_step"]
+    assert all(p in r["kernel_name"] for p in bench.KERNEL_PATTERNS["decode_f16_step"])
     assert any("FETCH_SIZE" in c for c in r["commands"]) and any("WRITE_SIZE" in c for c in r["commands"])
     assert r["bytes_per_launch"] > 0
 

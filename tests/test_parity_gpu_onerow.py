@@ -7,7 +7,7 @@ binary16 and bfloat16, from a single 512-wide load per row up to the largest K
 the kernel stages (32768) and just past it (the 16-row kernel then runs), with N
 ragged against the four rows of a workgroup.  The kernel adds its products in a
 fixed order of IEEE FP32 operations (per lane, eight running sums, then a fixed
-butterfly over the lanes): the acceptance rule of oracle/tolerance.py for random
+reduction over the lanes): the acceptance rule of oracle/tolerance.py for random
 data, bit for bit where the sums are exact, and bit for bit against the 16-row
 kernel on exact data.
 """

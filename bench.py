@@ -482,7 +482,8 @@ def _probe_lib():
     lib.probe_empty.argtypes = [i32, vp]
     lib.probe_mfma.argtypes = [vp, i32, i32, vp, vp]
     lib.probe_loads.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
-    for f in (lib.probe_read, lib.probe_empty, lib.probe_mfma, lib.probe_loads):
+    lib.probe_mfma_lds.argtypes = [vp, i32, i32, vp, vp]
+    for f in (lib.probe_read, lib.probe_empty, lib.probe_mfma, lib.probe_loads, lib.probe_mfma_lds):
         f.restype = i32
     return lib
 
@@ -496,6 +497,9 @@ def bench_probe(kind, torch, workloads, stream):
       empty: an empty kernel on that grid (the per-launch floor);
       mfma:  register-only v_mfma_f32_32x32x16_f16 on random binary16 operands
              (1024 workgroups of 4 waves, 2000 rounds of 8 MFMAs per wave);
+      mfma_lds: the attention projection's 512 tiles of 256 x 256 x 4096 with
+             their fragments read from LDS (random binary16 data loaded into
+             LDS once) and no operand loads from memory;
       loads_attn, loads_toy: the streaming GEMM's operand loads alone for the
              attention projection (256 x 256 tiles, 2 slots) and the toy layer
              (64 x 64 tiles, 4 slots), no fragment reads and no MFMAs, with the
@@ -526,6 +530,15 @@ def bench_probe(kind, torch, workloads, stream):
         def call(i):
             assert lib.probe_mfma(ops.data_ptr(), grid, iters, out.data_ptr(), sp) == 0
         calls, per = 8, 0
+    elif kind == "mfma_lds":
+        g = torch.Generator(device="cpu").manual_seed(3)
+        ops = torch.randn(4096 * 64 * 8, generator=g).to(torch.float16).to("cuda")
+        grid, nk = 512, 64
+        out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            assert lib.probe_mfma_lds(ops.data_ptr(), grid, nk, out.data_ptr(), sp) == 0
+        calls, per = 16, 0
     elif kind in ("loads_attn", "loads_toy"):
         name, tile, bm = ("attn", 0, 256) if kind == "loads_attn" else ("toy", 1, 64)
         wl = workloads.WORKLOADS[name]
@@ -545,7 +558,7 @@ def bench_probe(kind, torch, workloads, stream):
         raise SystemExit("unknown probe %s" % kind)
     graph = capture(call, calls, stream, torch)
     graph.replay()
-    replays = 4 if kind in ("mfma", "loads_attn") else max(1, 640 // calls)
+    replays = 4 if kind in ("mfma", "mfma_lds", "loads_attn") else max(1, 640 // calls)
     times = [time_region(graph, replays, stream, torch) for _ in range(5)]
     us = sorted(times)[2] / (replays * calls) * 1e3
     del graph
@@ -558,8 +571,8 @@ def bench_probe(kind, torch, workloads, stream):
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         r.update({"name": name, "tile": [bm, bm], "input_sets": sets, "bytes_into_cus_per_launch": per,
                   "gbs_per_cu": round(per / cus / (us * 1e-6) / 1e9, 1)})
-    if kind == "mfma":
-        flops = grid * 4 * iters * 8 * 32768.0
+    if kind in ("mfma", "mfma_lds"):
+        flops = grid * 4 * iters * 8 * 32768.0 if kind == "mfma" else grid * 8 * nk * 4 * 8 * 32768.0
         r.update({"flops_per_launch": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
                   "frac_mfma_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)})
     return r
@@ -703,7 +716,7 @@ def main():
     achieved = per_launch_bytes / per_launch_s / 1e9
     log("decode: %.3f us/step, %.1f GB/s" % (ms * 1e3, value))
     context = bench_context(torch, la, workloads, stream)
-    for kind in ("read", "empty", "mfma"):
+    for kind in ("read", "empty", "mfma", "mfma_lds"):
         log("probe", kind)
         context["probe_" + kind] = bench_probe(kind, torch, workloads, stream)
     # the decode launch's rate against a plain read of the same rotated weights on
@@ -725,6 +738,11 @@ def main():
             r["frac_of_call"] = round(r["us_per_launch"] / prefill[name]["us_per_call"], 4)
             prefill[name]["operand_loads_alone"] = r
             log(json.dumps(r))
+        # and attn's MFMAs with their fragments read from LDS, no operand loads
+        # (the same 512 tiles of work): what share of the call the matrix work is
+        m = dict(context["probe_mfma_lds"])
+        m["frac_of_call"] = round(m["us_per_launch"] / prefill["attn"]["us_per_call"], 4)
+        prefill["attn"]["mfma_fed_from_lds_alone"] = m
     variants = {}
     if not args.no_variants:
         dargs = argparse.Namespace(steps=args.steps, warmup=args.warmup, repeats=args.repeats)

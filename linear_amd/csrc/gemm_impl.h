@@ -1,7 +1,8 @@
 // gemm_impl.h -- MFMA tiled GEMM for the linear layer on gfx950 (templates).
 //
 // Computes the projection tile C[n, m] = sum_k weight[n, k] * x[m, k] with
-// v_mfma_f32_32x32x16_f16 / _bf16 (exact products, FP32 accumulation), then the
+// v_mfma_f32_32x32x16_f16 / _bf16, or v_mfma_f32_16x16x32_f16 / _bf16 on the
+// 256 x 256 streaming tile (exact products, FP32 accumulation), then the
 // contract's epilogue: round to the element type, and with a bias widen, add b[n]
 // in FP32 and round again ("tensor programs, part 1", section "One Program and One
 // Numerical Contract"; the Inductor capture's cast sequence; for bfloat16, "The
@@ -28,6 +29,8 @@
 // The streaming kernel (aligned layouts) and the register-staged one (any
 // layout) are described where they are defined below.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -225,23 +228,24 @@ __device__ inline void epi_tile(const LinearArgs& a, const unsigned char* tile, 
 }
 
 // The end of a streaming tile, after its last MFMA: the accumulators acc[i][j]
-// (32 x 32 blocks of wave (wm, wn), four consecutive output columns n of one row
-// m per lane and register group) leave through the LDS the ring used (RINGB
+// (R x R blocks of wave (wm, wn), R = 32 or 16; four consecutive output columns
+// n of one row m per lane and register group) leave through the LDS the ring used (RINGB
 // bytes, free again), in row order.  FP32 mode: the sums, staged as floats in
 // row bands when the tile is larger than the ring, 16-byte row stores.  Rounded
 // modes: the rounded tile staged as 16-bit words, then epi_tile (the bias or the
 // epilogue program, 16-byte row stores), with an epilogue program's first
 // activation table window copied into LDS behind the tile.
-template <int BM, int BN, int WM, int WN, int RINGB, int E, int MODE>
+template <int BM, int BN, int WM, int WN, int RINGB, int E, int MODE, int R, typename AccT>
 __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* smem,
-                                            f32x16 (&acc)[BN / WN / 32][BM / WM / 32], int m0, int n0, int wave,
+                                            AccT (&acc)[BN / WN / R][BM / WM / R], int m0, int n0, int wave,
                                             int lane, const u32x4* bias8 = nullptr) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int FM = TM / R, FN = TN / R;
+    constexpr int G = R * R / 256;                   // groups of 4 consecutive n per lane and block
     constexpr int TILEB = BM * BN * 2;
     const int wn = wave % WN, wm = wave / WN;
-    const int lr = lane & 31, lh = lane >> 5;
+    const int lr = lane % R, lh = lane / R;
     if constexpr (MODE == kOutF32) {
         // the FP32 sums go out the same way, staged as floats in the freed ring
         // (in row bands when the whole tile does not fit): row r of a band holds
@@ -249,7 +253,7 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
         constexpr int CPR4 = BN / 4;
         constexpr int PASSES = (BM * BN * 4 + RINGB - 1) / (RINGB);
         constexpr int RPP = BM / PASSES;                   // rows per band
-        static_assert(BM % PASSES == 0 && RPP % 32 == 0, "bands must hold whole 32-row fragment blocks");
+        static_assert(BM % PASSES == 0 && RPP % R == 0, "bands must hold whole fragment blocks");
         constexpr int CHT = RPP * CPR4 / NT;
         static_assert((RPP * CPR4) % NT == 0, "chunks must divide evenly over the threads");
 #pragma unroll
@@ -258,11 +262,11 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+                for (int g = 0; g < G; ++g) {
+                    const int nl = wn * TN + i * R + g * 8 + lh * 4;
 #pragma unroll
                     for (int j = 0; j < FM; ++j) {
-                        const int ml = wm * TM + j * 32 + lr - pass * RPP;
+                        const int ml = wm * TM + j * R + lr - pass * RPP;
                         if (ml >= 0 && ml < RPP) {
                             const f32x4 v = (f32x4){acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
                                                     acc[i][j][g * 4 + 3]};
@@ -320,11 +324,11 @@ __device__ __forceinline__ void finish_tile(const LinearArgs& a, unsigned char* 
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * TN + i * 32 + g * 8 + lh * 4;
+            for (int g = 0; g < G; ++g) {
+                const int nl = wn * TN + i * R + g * 8 + lh * 4;
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
-                    const int ml = wm * TM + j * 32 + lr;
+                    const int ml = wm * TM + j * R + lr;
                     uint2 u;
                     u.x = (uint32_t)narrow<E>(acc[i][j][g * 4]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 1]) << 16);
                     u.y = (uint32_t)narrow<E>(acc[i][j][g * 4 + 2]) | ((uint32_t)narrow<E>(acc[i][j][g * 4 + 3]) << 16);
@@ -388,13 +392,17 @@ __device__ inline void stream_tile(LinearArgs& a, int& tm, int& tn) {
 // once and its MFMAs run as they land; and only slices that exist are requested,
 // the wait for slice t choosing at run time how many later slices may still be
 // in flight (no zero-fill requests past K).
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1, bool WHOLE = false>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int MODE, int SPREAD = 1, bool WHOLE = false,
+          bool M16 = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_stream(LinearArgs a) {
-    constexpr int KS = BK / 16;                       // MFMA K steps per slice
+    constexpr int R = M16 ? 16 : 32;                  // MFMA block rows and columns
+    constexpr int KSTEP = M16 ? 32 : 16;              // k values per MFMA
+    constexpr int KS = BK / KSTEP;                    // MFMA K steps per slice
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int FM = TM / R, FN = TN / R;
+    using AccT = std::conditional_t<M16, f32x4, f32x16>;
     constexpr int ROWB = BK * 2;                      // bytes per LDS tile row
     constexpr int CPR = BK / 8;                       // 16-byte chunks per row
     constexpr int RP = 256 / ROWB;                    // rows per 256-byte span
@@ -405,7 +413,8 @@ gemm_stream(LinearArgs a) {
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(GROUPS % NW == 0, "row groups must divide evenly over the waves");
     static_assert(BN % RPL == 0, "weight rows must fill whole direct loads");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(TM % R == 0 && TN % R == 0, "wave tile must be a multiple of the MFMA block");
+    static_assert(WHOLE || KS % 2 == 0, "the pipelined loop alternates two fragment buffers per slice");
     static_assert(STAGES >= 2 && STAGES * SLICE <= 160 * 1024, "LDS ring too large");
     // after the main loop the ring holds the rounded tile (BM x BN words) and, for
     // an epilogue program, the LDS window of its first activation's table behind it
@@ -429,18 +438,27 @@ gemm_stream(LinearArgs a) {
     // latency is off the tile's tail: the epilogue gives thread t the row chunks
     // t, t + NT, ..., all at column n0 + 8 (t % (BN / 8)) since NT is a multiple
     // of BN / 8 (on the toy layer a bias load after the main loop cost ~1.3 us).
+    // The 16 x 16 x 32 loop has no registers to hold it through the K loop and
+    // requests it before its last slice instead.
     static_assert((NW * 64) % (BN / 8) == 0, "a thread's epilogue chunks must share their columns");
     u32x4 bias8 = (u32x4){0u, 0u, 0u, 0u};
-    if constexpr (MODE == kOutBias) {
+    auto request_bias = [&]() {
         const int c = n0 + 8 * ((int)threadIdx.x % (BN / 8));
         bias8 = load8(a.b + c, true, c, a.N, a.epi.vec16 & 2);
-    }
+    };
+    if constexpr (MODE == kOutBias && !M16) request_bias();
 
     // This wave's loads: groups g = wave * GPW + j; group g < BN / RPL holds weight
     // rows RPL g .., the others x rows.  Lane l fetches row l / CPR of the group,
-    // logical chunk (l % CPR) ^ ((row / RP) % CPR).
+    // logical chunk (l % CPR) ^ ((row / RP) % CPR).  (The whole offset stays in
+    // the lane's register: the range check that zero-fills rows past M or N
+    // looks at that part of the offset.)
+    // The chunk a lane fetches repeats every GPER groups (a wave's first group
+    // starts that period), so its first K element is kept once per phase.
+    constexpr int GPER = CPR / ((RPL / RP) < CPR ? (RPL / RP) : CPR);
+    static_assert((GPW * (RPL / RP)) % CPR == 0, "a wave's first group must start the swizzle's period");
     uint32_t goff[GPW];
-    int gk[GPW];                                   // first K element this lane fetches
+    int gk[GPER];                                  // first K element this lane fetches, per phase
 #pragma unroll
     for (int j = 0; j < GPW; ++j) {
         const int g = wave * GPW + j;
@@ -448,7 +466,7 @@ gemm_stream(LinearArgs a) {
         const int tr = g * RPL + lane / CPR;       // row within the slot (weight rows first)
         const int r = isw ? tr : tr - BN;          // row within its matrix tile
         const int c = (lane % CPR) ^ ((tr / RP) % CPR);
-        gk[j] = c * 8;
+        if (j < GPER) gk[j] = c * 8;
         goff[j] = (uint32_t)(((int64_t)r * (isw ? a.ldw : a.ldx) + c * 8) * 2);
     }
 
@@ -460,7 +478,7 @@ gemm_stream(LinearArgs a) {
         unsigned char* slot__ = smem + (t__ % STAGES) * SLICE;                           \
         const uint32_t kb__ = (uint32_t)(t__ * BK) * 2u;                                 \
         const int g__ = wave * GPW + (j_);                                               \
-        const bool kin__ = t__ * BK + gk[(j_)] < K;                                      \
+        const bool kin__ = t__ * BK + gk[(j_) % GPER] < K;                               \
         lds_dma16(g__ < BN / RPL ? rw : rx, slot__ + g__ * 1024, kin__ ? goff[(j_)] + kb__ : kOOB); \
     } while (0)
 
@@ -472,32 +490,35 @@ gemm_stream(LinearArgs a) {
     // (the window ends at least one K step before the barrier that waits for
     // these loads: SPREAD is capped at KS - 2)
     static_assert(SPREAD >= 0, "SPREAD counts K steps");
-    constexpr int SP = SPREAD < KS - 2 ? SPREAD : KS - 2;
+    constexpr int SP = SPREAD < KS - 2 ? SPREAD : (KS > 2 ? KS - 2 : 0);
     constexpr int DPS = (GPW + SP) / (1 + SP);
 
     const int wn = wave % WN, wm = wave / WN;
-    const int lr = lane & 31, lh = lane >> 5;
-    // byte offsets of this lane's fragment rows within a slot, per K step
-    uint32_t aoff[KS][FN], boff[KS][FM];
+    // lane l of a fragment holds row l % R and the 8 k values of chunk l / R of its K step
+    const int lr = lane % R, lh = lane / R;
+    // byte offsets of this lane's first A and B fragment rows within a slot, per
+    // K step.  Fragment i sits R i rows further down and R / RP is a multiple of
+    // CPR, so the swizzle term (r / RP) % CPR is the same for every fragment: the
+    // others are the first one's offset plus a constant (the read's immediate)
+    static_assert((R / RP) % CPR == 0, "fragment blocks must keep their rows' swizzle");
+    uint32_t aoff[KS], boff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int r = wn * TN + i * 32 + lr;
-            aoff[ks][i] = r * ROWB + (((ks * 2 + lh) ^ ((r / RP) % CPR)) << 4);
-        }
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int r = BN + wm * TM + j * 32 + lr;
-            boff[ks][j] = r * ROWB + (((ks * 2 + lh) ^ ((r / RP) % CPR)) << 4);
-        }
+        const int ra = wn * TN + lr, rb = BN + wm * TM + lr;
+        aoff[ks] = ra * ROWB + (((ks * (KSTEP / 8) + lh) ^ ((ra / RP) % CPR)) << 4);
+        boff[ks] = rb * ROWB + (((ks * (KSTEP / 8) + lh) ^ ((rb / RP) % CPR)) << 4);
     }
+    constexpr uint32_t FRAGB = R * ROWB;              // bytes between a wave's fragment blocks
+    auto mma = [](u32x4 x, u32x4 y, AccT c) {
+        if constexpr (M16) return mfma16x16x32<E>(x, y, c);
+        else return mfma32x32x16<E>(x, y, c);
+    };
 
-    f32x16 acc[FN][FM];
+    AccT acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
+        for (int j = 0; j < FM; ++j) acc[i][j] = (AccT){};
 
     if constexpr (WHOLE) {
         // at most c (< STAGES, uniform) slices' requests left in flight
@@ -523,9 +544,9 @@ gemm_stream(LinearArgs a) {
             u32x4 fa[KS][FN], fb[KS][FM];
             static_for<0, KS>([&]<int ks>() {
 #pragma unroll
-                for (int i = 0; i < FN; ++i) fa[ks][i] = *(const u32x4*)(slot + aoff[ks][i]);
+                for (int i = 0; i < FN; ++i) fa[ks][i] = *(const u32x4*)(slot + aoff[ks] + i * FRAGB);
 #pragma unroll
-                for (int j = 0; j < FM; ++j) fb[ks][j] = *(const u32x4*)(slot + boff[ks][j]);
+                for (int j = 0; j < FM; ++j) fb[ks][j] = *(const u32x4*)(slot + boff[ks] + j * FRAGB);
             });
             __builtin_amdgcn_sched_barrier(0);   // every read issued before the refill and the MFMAs
             if (t > 0 && t - 1 + STAGES < nk) static_for<0, GPW>([&]<int j>() { LIN_ISSUE_ONE(t - 1 + STAGES, j); });
@@ -534,7 +555,7 @@ gemm_stream(LinearArgs a) {
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
 #pragma unroll
-                    for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16<E>(fa[ks][i], fb[ks][j], acc[i][j]);
+                    for (int j = 0; j < FM; ++j) acc[i][j] = mma(fa[ks][i], fb[ks][j], acc[i][j]);
             });
         }
     } else if (nk > 0) {
@@ -550,24 +571,66 @@ gemm_stream(LinearArgs a) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW + DPS) : "memory");
         lds_barrier();   // slice 0 only: __syncthreads() would also wait for every later slice
 
+        if constexpr (M16) {
+        // 16 x 16 x 32 MFMAs (two K steps per 64-wide slice).  A wave's FN A
+        // fragments are double buffered and its FM B fragments single: each step
+        // runs its MFMAs B-fragment-major and reads the next step's B fragment j
+        // right after the FN MFMAs that use fragment j have been issued (the
+        // registers allow no second B buffer next to 128 accumulators).
+        static_assert(KS == 2, "the 16 x 16 x 32 loop takes 64-wide slices");
+        u32x4 a2[2][FN], b1[FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) a2[0][i] = *(const u32x4*)(smem + aoff[0] + i * FRAGB);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) b1[j] = *(const u32x4*)(smem + boff[0] + j * FRAGB);
+        // the MFMAs of the step held in buffer CUR while the step NKS of nslot is read
+        auto step = [&]<int CUR, int NKS>(const unsigned char* nslot) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) a2[CUR ^ 1][i] = *(const u32x4*)(nslot + aoff[NKS] + i * FRAGB);
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) acc[i][j] = mma(a2[CUR][i], b1[j], acc[i][j]);
+                b1[j] = *(const u32x4*)(nslot + boff[NKS] + j * FRAGB);
+            }
+        };
+        for (int t = 0; t + 1 < nk; ++t) {
+            step.template operator()<0, 1>(smem + (t % STAGES) * SLICE);
+            order_step16<FN, FM, 0>();
+            // slice t + 1 has landed and every wave has read slot t's last step
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * GPW) : "memory");
+            lds_barrier();
+            step.template operator()<1, 0>(smem + ((t + 1) % STAGES) * SLICE);
+            static_for<0, GPW>([&]<int j>() { LIN_ISSUE_ONE(t + STAGES, j); });
+            order_step16<FN, FM, GPW>();
+        }
+        if constexpr (MODE == kOutBias) request_bias();
+        step.template operator()<0, 1>(smem + ((nk - 1) % STAGES) * SLICE);
+        order_step16<FN, FM, 0>();
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int i = 0; i < FN; ++i) acc[i][j] = mma(a2[1][i], b1[j], acc[i][j]);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
         u32x4 af[2][FN], bf[2][FM];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) af[0][i] = *(const u32x4*)(smem + aoff[0][i]);
+        for (int i = 0; i < FN; ++i) af[0][i] = *(const u32x4*)(smem + aoff[0] + i * FRAGB);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) bf[0][j] = *(const u32x4*)(smem + boff[0][j]);
+        for (int j = 0; j < FM; ++j) bf[0][j] = *(const u32x4*)(smem + boff[0] + j * FRAGB);
 
         auto read_frags = [&](const unsigned char* slot, int ks, int buf) {
 #pragma unroll
-            for (int i = 0; i < FN; ++i) af[buf][i] = *(const u32x4*)(slot + aoff[ks][i]);
+            for (int i = 0; i < FN; ++i) af[buf][i] = *(const u32x4*)(slot + aoff[ks] + i * FRAGB);
 #pragma unroll
-            for (int j = 0; j < FM; ++j) bf[buf][j] = *(const u32x4*)(slot + boff[ks][j]);
+            for (int j = 0; j < FM; ++j) bf[buf][j] = *(const u32x4*)(slot + boff[ks] + j * FRAGB);
         };
         auto mfmas = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j)
-                    acc[i][j] = mfma32x32x16<E>(af[buf][i], bf[buf][j], acc[i][j]);
+                    acc[i][j] = mma(af[buf][i], bf[buf][j], acc[i][j]);
         };
         // K steps 0 .. KS-2 of slice t: read the next step while this one
         // multiplies; the first SP steps also issue the deferred loads of
@@ -601,10 +664,11 @@ gemm_stream(LinearArgs a) {
         mfmas((KS - 1) & 1);
         // the zero-fill requests past the end must land before the LDS is released
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
     }
 #undef LIN_ISSUE_ONE
-    finish_tile<BM, BN, WM, WN, STAGES * SLICE, E, MODE>(a, smem, acc, m0, n0, wave, lane,
-                                                        MODE == kOutBias ? &bias8 : nullptr);
+    finish_tile<BM, BN, WM, WN, STAGES * SLICE, E, MODE, R>(a, smem, acc, m0, n0, wave, lane,
+                                                           MODE == kOutBias ? &bias8 : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -618,12 +682,14 @@ static const void* regstaged_fn(int mode) {
     return (const void*)gemm_kernel<BM, BN, WM, WN, E, kOutF32>;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD, bool WHOLE = false>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int E, int SPREAD, bool WHOLE = false, bool M16 = false>
 static const void* stream_fn(int mode) {
-    if (mode == kOutBias) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD, WHOLE>;
-    if (mode == kOutRound) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD, WHOLE>;
-    if (mode == kOutEpi) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutEpi, SPREAD, WHOLE>;
-    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD, WHOLE>;
+    if (mode == kOutBias)
+        return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutBias, SPREAD, WHOLE, M16>;
+    if (mode == kOutRound)
+        return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutRound, SPREAD, WHOLE, M16>;
+    if (mode == kOutEpi) return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutEpi, SPREAD, WHOLE, M16>;
+    return (const void*)gemm_stream<BM, BN, WM, WN, STAGES, BK, E, kOutF32, SPREAD, WHOLE, M16>;
 }
 
 static hipError_t launch(const void* fn, const LinearArgs& a, int threads, hipStream_t stream) {
@@ -649,8 +715,11 @@ hipError_t launch_gemm_stream_t(int cfg, const LinearArgs& a, int mode, hipStrea
         // with the ring's own barriers: 256 x 256 best at 1, 256 x 128 and 128 x 128
         // at 2 (down 241 -> 222 us); 128 x 256 (32-wide slices) has no step to
         // spare.  64 x 64 reads whole slices (toy layer: 6.94 us per call against
-        // 7.17 pipelined; rings of 3, 5 or 6 slots 7.6-8.1)
-        case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E, 1>(mode), a, 512, stream);
+        // 7.17 pipelined; rings of 3, 5 or 6 slots 7.6-8.1).  The 256 x 256 tile
+        // multiplies with 16 x 16 x 32 MFMAs (attn 232 -> 226 us, mlp_up 408 ->
+        // 400); the smaller tiles measured slower with them (down +4%, 128 x 128
+        // +15%) and keep 32 x 32 x 16
+        case 0: return launch(stream_fn<256, 256, 2, 4, 2, 64, E, 1, false, true>(mode), a, 512, stream);
         case 1: return launch(stream_fn<256, 128, 4, 2, 3, 64, E, 2>(mode), a, 512, stream);
         case 2: return launch(stream_fn<128, 256, 2, 4, 4, 32, E, 0>(mode), a, 512, stream);
         case 3: return launch(stream_fn<128, 128, 2, 2, 4, 64, E, 2>(mode), a, 256, stream);

@@ -54,4 +54,22 @@ __device__ __forceinline__ void order_step() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Instruction order of one K step of the 16 x 16 x 32 streaming loop: its first
+// MFMA, the FN A-fragment reads of the next step, the rest of B fragment 0's
+// MFMAs, then for each B fragment j its next-step read, one of the ND loads while
+// any are left, and fragment j + 1's FN MFMAs.
+template <int FN, int FM, int ND>
+__device__ __forceinline__ void order_step16() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FN, 0);
+    if constexpr (FN > 1) __builtin_amdgcn_sched_group_barrier(0x008, FN - 1, 0);
+    static_for<0, FM>([&]<int j>() {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (j < ND) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        if constexpr (j + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+    });
+    if constexpr (ND > FM) __builtin_amdgcn_sched_group_barrier(0x010, ND - FM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace lin

@@ -13,11 +13,11 @@
 //    64-wide K slices, its direct-to-LDS loads, waits, barriers and XCD tile walk,
 //    no fragment reads and no MFMAs): how fast the operands of a tile reach a CU.
 //  - probe_mfma_lds: the 256 x 256 tile's MFMAs fed from LDS with no operand loads
-//    from memory: 8 waves of 128 x 64, each K step's 6 fragments read from a
-//    two-slot ring of 64-wide slices (filled once with random binary16 data, the
-//    streaming GEMM's swizzle, so the reads are free of bank conflicts) while the
-//    previous step's 8 MFMAs run, and a barrier per slice: what the tile's matrix
-//    work costs once its operands are in LDS.
+//    from memory: 8 waves of 128 x 64, each 32-wide K step's 12 fragments read
+//    from a two-slot ring of 64-wide slices (filled once with random binary16
+//    data, the streaming GEMM's swizzle, so the reads are free of bank conflicts)
+//    while the previous step's 32 v_mfma_f32_16x16x32_f16 run, and a barrier per
+//    slice: what the tile's matrix work costs once its operands are in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,6 +26,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kUnroll = 16;   // loads per thread in flight at once
@@ -168,11 +169,12 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(const u32x4* ops, int i
 // One 256 x 256 tile's K loop with its operands already in LDS.  LDS holds two
 // slots of a 64-wide K slice: 256 weight rows then 256 x rows of 128 bytes, the
 // 16-byte chunk c of row r at chunk c ^ ((r / 2) % 8).  Wave (wm, wn) of the 2 x 4
-// grid owns x rows wm * 128 .. +128 and weight rows wn * 64 .. +64: per 16-wide K
-// step it reads 2 weight and 4 x fragments (lane l: row l % 32, chunk 2 step +
-// l / 32) and runs 8 v_mfma_f32_32x32x16_f16; the next step's fragments are read
-// while this step's MFMAs run.  nk slices, a barrier after each.  Each lane's
-// accumulators are added into out[blockIdx.x * 512 + threadIdx.x].
+// grid owns x rows wm * 128 .. +128 and weight rows wn * 64 .. +64: per 32-wide K
+// step it reads 4 weight and 8 x fragments (lane l: row l % 16, chunk 4 step +
+// l / 16) and runs 32 v_mfma_f32_16x16x32_f16, as the layer's 256 x 256 tile
+// does; the next step's fragments are read while this step's MFMAs run.  nk
+// slices, a barrier after each.  Each lane's accumulators are added into
+// out[blockIdx.x * 512 + threadIdx.x].
 __global__ void __launch_bounds__(512) probe_mfma_lds_kernel(const u32x4* ops, int nk, float* out) {
     constexpr int SLICE = 512 * 128;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLICE];
@@ -185,46 +187,46 @@ __global__ void __launch_bounds__(512) probe_mfma_lds_kernel(const u32x4* ops, i
     }
     __syncthreads();
     auto frag = [&](int slot, int row, int step) -> f16x8 {
-        const int c = 2 * step + (lane >> 5);
-        const int r = row + (lane & 31);
+        const int c = 4 * step + (lane >> 4);
+        const int r = row + (lane & 15);
         return __builtin_bit_cast(f16x8, *(const u32x4*)(smem + slot * SLICE + r * 128 + ((c ^ ((r >> 1) & 7)) << 4)));
     };
-    f32x16 acc[2][4];
+    f32x4 acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-    f16x8 a[2][2], b[2][4];
+        for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){};
+    f16x8 a[2][4], b[2][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[0][i] = frag(0, wn * 64 + i * 32, 0);
+    for (int i = 0; i < 4; ++i) a[0][i] = frag(0, wn * 64 + i * 16, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[0][j] = frag(0, 256 + wm * 128 + j * 32, 0);
+    for (int j = 0; j < 8; ++j) b[0][j] = frag(0, 256 + wm * 128 + j * 16, 0);
     for (int t = 0; t < nk; ++t) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;
             // the next step's fragments (the next slice's first step after the last)
-            const int nslot = ks < 3 ? (t & 1) : ((t + 1) & 1);
-            const int nstep = (ks + 1) & 3;
+            const int nslot = ks < 1 ? (t & 1) : ((t + 1) & 1);
+            const int nstep = (ks + 1) & 1;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[nxt][i] = frag(nslot, wn * 64 + i * 32, nstep);
+            for (int i = 0; i < 4; ++i) a[nxt][i] = frag(nslot, wn * 64 + i * 16, nstep);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[nxt][j] = frag(nslot, 256 + wm * 128 + j * 32, nstep);
+            for (int j = 0; j < 8; ++j) b[nxt][j] = frag(nslot, 256 + wm * 128 + j * 16, nstep);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sum += acc[i][j][e];
+            for (int e = 0; e < 4; ++e) sum += acc[i][j][e];
     out[(int64_t)blockIdx.x * 512 + tid] = sum;
 }
 
@@ -287,7 +289,7 @@ int32_t probe_mfma(const void* ops, int32_t grid, int32_t iters, float* out, voi
 }
 
 // ops: 4096 * 64 16-byte words (4 MiB) of operand data; out: grid * 512 floats.
-// FLOPs per call: grid * 8 waves * nk slices * 4 steps * 8 MFMAs * 32768, i.e. a
+// FLOPs per call: grid * 8 waves * nk slices * 2 steps * 32 MFMAs * 16384, i.e. a
 // 256 x 256 x 64 nk tile per workgroup.
 int32_t probe_mfma_lds(const void* ops, int32_t grid, int32_t nk, float* out, void* stream) {
     if (!ops || !out || grid <= 0 || nk <= 0) return -1;

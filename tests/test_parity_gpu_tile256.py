@@ -1,0 +1,97 @@
+"""The 256 x 256 streaming tile (16 x 16 x 32 MFMAs) at ragged shapes, every
+output, both element types, every output mode (needs a gfx950 GPU).
+
+The other streaming tiles multiply with 32 x 32 x 16 MFMAs.  Both shapes feed
+each output the same 16-wide k groups in the same order, so a layer gives the
+same bits whichever tile computes it: here the rows of a 256 x 256-tile call are
+compared with the same rows computed alone (a 64 x 64-tile call).  Against the
+oracle: the acceptance rule of oracle/tolerance.py on random data, bit for bit
+on integer data ("tensor programs, part 1", section "One Program and One
+Numerical Contract").
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_amd as la
+from linear_amd import workloads
+from test_parity_gpu_variants import BF, F16, DEV, full_check, words, eq_words, elem_of
+
+pytestmark = pytest.mark.gpu
+
+# M and N ragged against 256, K ragged against the 64-wide slices
+SHAPES = [(4000, 4000, 72), (4096, 4000, 200), (3900, 4096, 8)]
+
+
+def inputs(M, N, K, dtype, seed, integers=False):
+    if integers:
+        x, w, b = workloads.small_integers(M, N, K, seed=seed)
+        return x.to(dtype), w.to(dtype), b.to(dtype)
+    return workloads.make_inputs(M, N, K, 1.0 / np.sqrt(K), seed=seed, dtype=dtype)
+
+
+def assert_tile(x, w, b):
+    p = la.linear_f16_plan(x.to(F16), w.to(F16), b.to(F16))
+    assert (p["tile_m"], p["tile_n"], p["split_n"]) == (256, 256, 0), p
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", SHAPES, ids=["%dx%dx%d" % s for s in SHAPES])
+def test_tile256_random_every_output(orc, M, N, K, dtype):
+    x, w, b = inputs(M, N, K, dtype, seed=M + N + K)
+    assert_tile(x, w, b)
+    full_check(orc, x, w, b, la.PATH_AUTO, dtype)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_tile256_integers_bit_exact(orc, dtype):
+    x, w, b = inputs(4000, 4000, 72, dtype, seed=5, integers=True)
+    assert_tile(x, w, b)
+    full_check(orc, x, w, b, la.PATH_AUTO, dtype, exact=True)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_tile256_rows_equal_the_small_tile_call(dtype):
+    """Rows 0..63 and the last 37 rows of a 256 x 256-tile call against the same
+    rows computed alone (64 x 64 tiles, 32 x 32 x 16 MFMAs): the same words, with
+    and without the bias, and the same FP32 sums."""
+    M, N, K = 4000, 4000, 200
+    x, w, b = inputs(M, N, K, dtype, seed=11)
+    assert_tile(x, w, b)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    lin = la.linear_bf16 if dtype == BF else la.linear_f16
+    nob = la.linear_bf16_nobias if dtype == BF else la.linear_f16_nobias
+    f32 = la.linear_bf16_f32out if dtype == BF else la.linear_f16_f32out
+    y, p, s = lin(xd, wd, bd), nob(xd, wd), f32(xd, wd)
+    for rows in (slice(0, 64), slice(M - 37, M)):
+        xs = xd[rows].contiguous()
+        plan = la.linear_f16_plan(xs.to(F16), wd.to(F16), bd.to(F16))
+        assert (plan["tile_m"], plan["tile_n"]) != (256, 256), plan
+        ys, ps, ss = lin(xs, wd, bd), nob(xs, wd), f32(xs, wd)
+        torch.cuda.synchronize()
+        assert np.array_equal(words(ys), words(y[rows]))
+        assert np.array_equal(words(ps), words(p[rows]))
+        assert np.array_equal(ss.cpu().numpy().view(np.uint32), s[rows].cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_tile256_epilogue_program_equals_the_bias_call(dtype):
+    """The epilogue-program kernel of the 256 x 256 tile with the bias step alone
+    gives the bias call's words; with the bias, a residual and the gate multiply
+    each step is applied to the rounded value of the step before."""
+    M, N, K = 4000, 4000, 72
+    x, w, b = inputs(M, N, K, dtype, seed=13)
+    assert_tile(x, w, b)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    g = torch.Generator().manual_seed(14)
+    r = torch.randn(M, N, generator=g).to(dtype).to(DEV)
+    m = torch.randn(M, N, generator=g).to(dtype).to(DEV)
+    lin = la.linear_bf16 if dtype == BF else la.linear_f16
+    epi = la.linear_bf16_epilogue if dtype == BF else la.linear_f16_epilogue
+    y = lin(xd, wd, bd)
+    e1 = epi(xd, wd, [la.EPI_BIAS], bias=bd)
+    e3 = epi(xd, wd, [la.EPI_BIAS, la.EPI_RESIDUAL, la.EPI_MUL], bias=bd, residual=r, mul=m)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(e1), words(y))
+    want = ((y.float() + r.float()).to(dtype).float() * m.float()).to(dtype)
+    assert eq_words(words(e3), words(want), elem_of(dtype)).all()

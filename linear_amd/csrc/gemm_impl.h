@@ -446,7 +446,8 @@ gemm_stream(LinearArgs a) {
         const int c = n0 + 8 * ((int)threadIdx.x % (BN / 8));
         bias8 = load8(a.b + c, true, c, a.N, a.epi.vec16 & 2);
     };
-    if constexpr (MODE == kOutBias && !M16) request_bias();
+    constexpr bool LATE_BIAS = M16 && !WHOLE;        // requested after the K loop instead
+    if constexpr (MODE == kOutBias && !LATE_BIAS) request_bias();
 
     // This wave's loads: groups g = wave * GPW + j; group g < BN / RPL holds weight
     // rows RPL g .., the others x rows.  Lane l fetches row l / CPR of the group,
@@ -667,6 +668,10 @@ gemm_stream(LinearArgs a) {
         }
     }
 #undef LIN_ISSUE_ONE
+    // with no K slice at all the 16 x 16 x 32 loop did not run: the bias chunk still goes in
+    if constexpr (MODE == kOutBias && LATE_BIAS) {
+        if (nk == 0) request_bias();
+    }
     finish_tile<BM, BN, WM, WN, STAGES * SLICE, E, MODE, R>(a, smem, acc, m0, n0, wave, lane,
                                                            MODE == kOutBias ? &bias8 : nullptr);
 }

@@ -95,3 +95,29 @@ def test_tile256_epilogue_program_equals_the_bias_call(dtype):
     assert np.array_equal(words(e1), words(y))
     want = ((y.float() + r.float()).to(dtype).float() * m.float()).to(dtype)
     assert eq_words(words(e3), words(want), elem_of(dtype)).all()
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+def test_tile256_k0_is_the_empty_sum(dtype):
+    """K = 0 at a shape that takes the 256 x 256 tile: no K slice runs, the sums
+    are +0, the projection is +0 and y is the bias ("tensor programs, part 1",
+    the layer's definition with an empty sum)."""
+    M, N = 4096, 4096
+    # zero-width views of 8-column matrices: row strides of 8 elements, so the
+    # call takes the 16-byte streaming kernels (a bare [M, 0] tensor would not)
+    x = torch.zeros(M, 8, dtype=dtype)[:, :0]
+    w = torch.zeros(N, 8, dtype=dtype)[:, :0]
+    b = workloads.make_inputs(1, N, 8, 0.5, seed=21, dtype=dtype)[2]
+    assert_tile(x, w, b)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    lin = la.linear_bf16 if dtype == BF else la.linear_f16
+    nob = la.linear_bf16_nobias if dtype == BF else la.linear_f16_nobias
+    f32 = la.linear_bf16_f32out if dtype == BF else la.linear_f16_f32out
+    epi = la.linear_bf16_epilogue if dtype == BF else la.linear_f16_epilogue
+    y, p, s, e = lin(xd, wd, bd), nob(xd, wd), f32(xd, wd), epi(xd, wd, [la.EPI_BIAS], bias=bd)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(words(b)[None, :], (M, N))
+    assert eq_words(words(y), want, elem_of(dtype)).all()
+    assert eq_words(words(e), want, elem_of(dtype)).all()
+    assert (words(p) == 0).all()
+    assert (s.cpu().numpy().view(np.uint32) == 0).all()

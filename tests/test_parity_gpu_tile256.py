@@ -1,5 +1,6 @@
 """The 256 x 256 streaming tile (16 x 16 x 32 MFMAs) at ragged shapes, every
-output, both element types, every output mode (needs a gfx950 GPU).
+output, both element types, every output mode; and K = 0 on every streaming tile
+and every remainder tile of the column split (needs a gfx950 GPU).
 
 The other streaming tiles multiply with 32 x 32 x 16 MFMAs.  Both shapes feed
 each output the same 16-wide k groups in the same order, so a layer gives the
@@ -120,4 +121,37 @@ def test_tile256_k0_is_the_empty_sum(dtype):
     assert eq_words(words(y), want, elem_of(dtype)).all()
     assert eq_words(words(e), want, elem_of(dtype)).all()
     assert (words(p) == 0).all()
+    assert (s.cpu().numpy().view(np.uint32) == 0).all()
+
+
+# shapes the host planner sends to each streaming tile and each remainder tile of
+# the column split: (M, N, tile, split remainder tile or None)
+K0_SHAPES = [(1282, 5377, (256, 128), None), (5428, 1281, (128, 256), None), (4612, 775, (128, 128), None),
+             (605, 619, (64, 64), None), (3877, 4109, (256, 256), (64, 64)), (3986, 5010, (256, 256), (128, 128)),
+             (4002, 5914, (256, 256), (128, 256)), (3896, 6060, (256, 256), (256, 128))]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("M,N,tile,rest", K0_SHAPES, ids=["%dx%d" % s[:2] for s in K0_SHAPES])
+def test_every_streaming_tile_k0_is_the_empty_sum(M, N, tile, rest, dtype):
+    """K = 0 on each streaming tile: every output of the bias call and of the
+    one-step bias program is the bias word, the projection and the FP32 sums +0
+    (the layer's definition with an empty sum)."""
+    x = torch.zeros(M, 8, dtype=dtype)[:, :0]
+    w = torch.zeros(N, 8, dtype=dtype)[:, :0]
+    b = workloads.make_inputs(1, N, 8, 0.5, seed=M + N, dtype=dtype)[2]
+    p = la.linear_f16_plan(x.view(F16), w.view(F16), b.view(F16))
+    assert (p["tile_m"], p["tile_n"]) == tile, p
+    assert ((p["tile_m2"], p["tile_n2"]) if p["split_n"] else None) == rest, p
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    lin = la.linear_bf16 if dtype == BF else la.linear_f16
+    nob = la.linear_bf16_nobias if dtype == BF else la.linear_f16_nobias
+    f32 = la.linear_bf16_f32out if dtype == BF else la.linear_f16_f32out
+    epi = la.linear_bf16_epilogue if dtype == BF else la.linear_f16_epilogue
+    y, pr, s, e = lin(xd, wd, bd), nob(xd, wd), f32(xd, wd), epi(xd, wd, [la.EPI_BIAS], bias=bd)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(words(b)[None, :], (M, N))
+    assert eq_words(words(y), want, elem_of(dtype)).all()
+    assert eq_words(words(e), want, elem_of(dtype)).all()
+    assert (words(pr) == 0).all()
     assert (s.cpu().numpy().view(np.uint32) == 0).all()

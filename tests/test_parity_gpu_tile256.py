@@ -1,6 +1,7 @@
 """The 256 x 256 streaming tile (16 x 16 x 32 MFMAs) at ragged shapes, every
-output, both element types, every output mode; and K = 0 on every streaming tile
-and every remainder tile of the column split (needs a gfx950 GPU).
+output, both element types, every output mode; K = 0 on every streaming tile
+and every remainder tile of the column split; NaN, infinities and overflow on the
+larger tiles (needs a gfx950 GPU).
 
 The other streaming tiles multiply with 32 x 32 x 16 MFMAs.  Both shapes feed
 each output the same 16-wide k groups in the same order, so a layer gives the
@@ -16,6 +17,7 @@ import torch
 
 import linear_amd as la
 from linear_amd import workloads
+from oracle import tolerance
 from test_parity_gpu_variants import BF, F16, DEV, full_check, words, eq_words, elem_of
 
 pytestmark = pytest.mark.gpu
@@ -155,3 +157,52 @@ def test_every_streaming_tile_k0_is_the_empty_sum(M, N, tile, rest, dtype):
     assert eq_words(words(e), want, elem_of(dtype)).all()
     assert (words(pr) == 0).all()
     assert (s.cpu().numpy().view(np.uint32) == 0).all()
+
+
+SPECIAL_SHAPES = [(1282, 5377), (5428, 1281), (4612, 775), (4002, 5914)]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF], ids=["f16", "bf16"])
+@pytest.mark.parametrize("M,N", SPECIAL_SHAPES, ids=["%dx%d" % s for s in SPECIAL_SHAPES])
+def test_specials_on_the_large_tiles(orc, M, N, dtype):
+    """A NaN in x row 5 makes row 5 NaN; +inf in weight row 7 (against x values
+    of 1) makes column 7 +inf; +inf and -inf in weight row 9 make column 9 NaN;
+    x row 11 times a column of 4s at 60000 overflows binary16 (not bfloat16).
+    The special class of every output equals the oracle's, and every finite
+    output satisfies the acceptance rule ("tensor programs, part 1", section
+    "One Program and One Numerical Contract": IEEE arithmetic throughout)."""
+    K = 72
+    elem = elem_of(dtype)
+    x, w, b = inputs(M, N, K, dtype, seed=M + 3 * N)
+    x[:, 10] = 1.0
+    x[:, 20] = 1.0
+    x[:, 21] = 1.0
+    x[5, 3] = float("nan")
+    w[7, 10] = float("inf")
+    w[9, 20] = float("inf")
+    w[9, 21] = float("-inf")
+    x[11, 30] = 60000.0
+    w[:, 30] = 4.0
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    lin = la.linear_bf16 if dtype == BF else la.linear_f16
+    nob = la.linear_bf16_nobias if dtype == BF else la.linear_f16_nobias
+    y, p = words(lin(xd, wd, bd)), words(nob(xd, wd))
+    torch.cuda.synchronize()
+    y_ref, p_ref = orc.linear(x, w, b, elem=elem)
+    for got, ref in ((p, p_ref), (y, y_ref)):
+        g, r = tolerance.words_to_f64(got, elem), tolerance.words_to_f64(ref, elem)
+        assert np.array_equal(np.isnan(g), np.isnan(r)), "NaN outputs differ"
+        assert np.array_equal(np.isposinf(g), np.isposinf(r)) and np.array_equal(np.isneginf(g), np.isneginf(r))
+    r = tolerance.words_to_f64(p_ref, elem)
+    assert np.isnan(r[5]).all() and np.isnan(r[:, 9]).all() and np.isposinf(r[np.arange(M) != 5, 7]).all()
+    rest = np.ones(N, bool)
+    rest[[7, 9]] = False
+    # row 11 sums to about 240000: past binary16's range, inside bfloat16's
+    assert (np.isposinf(r[11, rest]) if dtype == F16 else np.isfinite(r[11, rest])).all()
+    fin = np.isfinite(r)
+    _, A = orc.band(x, w, elem=elem)
+    ok, rep = tolerance.check_proj(p[fin], p_ref[fin], A[fin], elem=elem)
+    assert ok.all(), rep
+    fy = fin & np.isfinite(tolerance.words_to_f64(y_ref, elem))
+    ok, rep = tolerance.check_y(y[fy], y_ref[fy], p_ref[fy], A[fy], elem=elem)
+    assert ok.all(), rep
